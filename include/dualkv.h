@@ -1,0 +1,136 @@
+/*
+ * dualkv.h -- C ABI of the shared-prompt (DualKV) attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is defined in "DualKV: Shared-Prompt Flash Attention for
+ * Efficient RL Training with Large Rollouts and Long Contexts" (arXiv
+ * 2605.15422), Abstract: N response sequences of R tokens share one prompt
+ * of P tokens.  The N(P+R) tokens of such a micro-batch are repacked into
+ * P+NR tokens; prompt queries attend causally within the prompt, and each
+ * response query attends to the whole prompt plus its own response
+ * (causally) under one softmax spanning both key regions.  The result is
+ * exactly standard causal attention on the N replicated sequences.
+ *
+ * Layouts (all row-major, contiguous, no padding between rows):
+ *   packed rows   t = 0 .. T-1, T = P + N*R:
+ *                 rows 0..P-1 are the prompt; rows P+n*R .. P+n*R+R-1 are
+ *                 response n (n = 0..N-1).
+ *   replicated    N sequences of P+R rows: sequence n = [prompt; response n].
+ *   Q, O, dO, dQ  [T, Hq, D]   (element type: dualkv_params.dtype)
+ *   K, V, dK, dV  [T, Hkv, D]
+ *   LSE           [Hq, T]      fp32, natural log of sum_j exp(scale*q.k_j)
+ *
+ * Positions: response token r has logical position P+r; causality and the
+ * sliding window use logical positions.  Causal is inclusive (a token sees
+ * itself).  A window W > 0 keeps keys with 0 <= pos_q - pos_k < W.
+ * GQA: query head h reads KV head h / (Hq/Hkv).
+ * Response rows r >= valid_len[n] are padding: masked as queries (O = 0,
+ * LSE = -inf, dQ = 0) and as keys (dK = dV = 0 on those rows).
+ *
+ * Ownership: every pointer is caller-owned device memory (except `p`, a
+ * host pointer).  The library never allocates or frees memory, keeps no
+ * pointer after a call returns, and holds no mutable global state.
+ * Streams: `stream` is a hipStream_t (NULL = default stream); all work is
+ * enqueued on it and the call returns after enqueueing.
+ * Errors: arguments are validated on the host before anything is
+ * launched; on a non-zero return nothing was launched and no output was
+ * written.  DUALKV_ERR_HIP reports a failure of the HIP runtime at launch.
+ * Outputs must not alias inputs.
+ */
+#ifndef DUALKV_H
+#define DUALKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DUALKV_OK = 0,
+  DUALKV_ERR_INVALID_ARGUMENT = 1,
+  DUALKV_ERR_UNSUPPORTED = 2,
+  DUALKV_ERR_WORKSPACE_TOO_SMALL = 3,
+  DUALKV_ERR_HIP = 4
+};
+
+enum { DUALKV_F32 = 0, DUALKV_BF16 = 1 };        /* dualkv_params.dtype */
+enum { DUALKV_GATHER = 0, DUALKV_SCATTER = 1 };  /* dualkv_repack direction */
+enum {                                            /* dualkv_params.impl */
+  DUALKV_IMPL_AUTO = 0,     /* MFMA tiles when supported, else scalar */
+  DUALKV_IMPL_SCALAR = 1,   /* one wavefront per row, fp32 arithmetic */
+  DUALKV_IMPL_MFMA = 2      /* bf16 MFMA tiles; UNSUPPORTED if not possible */
+};
+
+typedef struct dualkv_params {
+  int32_t n_resp;        /* N >= 1 */
+  int32_t prompt_len;    /* P >= 0 (P = 0: N independent causal sequences) */
+  int32_t resp_len;      /* R >= 0, padded response length */
+  int32_t n_q_heads;     /* Hq >= 1 */
+  int32_t n_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;      /* D: 1..512 (scalar); 64, 128, 256, 512 (MFMA) */
+  int32_t window;        /* <= 0: none; else keys with pos_q - pos_k < window */
+  float softmax_scale;   /* 0: 1/sqrt(D) */
+  int32_t dtype;         /* DUALKV_F32 or DUALKV_BF16, shared by every tensor
+                            argument except LSE (always fp32) */
+  int32_t impl;          /* DUALKV_IMPL_* */
+  const int32_t* resp_valid_len;  /* device int32 [N] or NULL (= all R);
+                                     values are clamped to [0, R] */
+} dualkv_params;
+
+/*
+ * Repack rows between the replicated N(P+R) layout and the packed P+NR
+ * layout (arXiv 2605.15422, Abstract: the data-pipeline repack).
+ *   DUALKV_GATHER : src replicated [N(P+R) rows] -> dst packed [P+NR rows];
+ *                   the prompt is taken from copy 0.
+ *   DUALKV_SCATTER: src packed -> dst replicated; the prompt is copied into
+ *                   every sequence.
+ * Rows are opaque: row_bytes >= 1 bytes each (any element type, any head
+ * count).  The copy is bit exact.  src and dst must not overlap.
+ * Returns DUALKV_ERR_INVALID_ARGUMENT for null pointers (with a non-empty
+ * copy), row_bytes < 1, N < 1, P < 0, R < 0 or an unknown direction.
+ */
+int dualkv_repack(const void* src, void* dst, int64_t row_bytes,
+                  int32_t n_resp, int32_t prompt_len, int32_t resp_len,
+                  int32_t direction, void* stream);
+
+/*
+ * Forward pass over the packed layout (arXiv 2605.15422, Abstract: one
+ * kernel launch iterates over the two disjoint key regions, shared prompt
+ * and own response).  Reads q, k, v; writes o [T, Hq, D] (dtype) and
+ * lse [Hq, T] (fp32).  Rows with no visible key get O = 0, LSE = -inf.
+ */
+int dualkv_fwd(const dualkv_params* p, const void* q, const void* k,
+               const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace dualkv_bwd needs for these parameters
+ * (per-row softmax statistics and the split partial sums of the prompt
+ * dK/dV).  Returns 0 when the parameters are invalid.
+ */
+size_t dualkv_bwd_workspace_bytes(const dualkv_params* p);
+
+/*
+ * Backward pass (arXiv 2605.15422, Abstract: fused backward over the two
+ * key regions).  Given q, k, v, the forward's o and lse, and dout (dO),
+ * overwrites dq [T, Hq, D], dk and dv [T, Hkv, D].  The prompt rows of
+ * dk/dv hold the sum over the prompt's own queries and all N responses;
+ * that sum is accumulated in a fixed order, so results are bitwise
+ * reproducible run to run.  `workspace` must hold at least
+ * dualkv_bwd_workspace_bytes(p) bytes (DUALKV_ERR_WORKSPACE_TOO_SMALL
+ * otherwise) and be 256-byte aligned; its contents on entry are ignored.
+ */
+int dualkv_bwd(const dualkv_params* p, const void* q, const void* k,
+               const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* dualkv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUALKV_H */

@@ -1,0 +1,182 @@
+"""Python binding of libdualkv.so (shared-prompt / DualKV attention on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of the
+library.  torch supplies device memory and the current stream.  The
+functions carry the names of the C entry points declared in
+include/dualkv.h; see that header for layouts, masks and errors.
+
+There is no fallback: if the library is not built, or a call fails, a
+RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdualkv.so")
+
+DUALKV_OK = 0
+DUALKV_F32, DUALKV_BF16 = 0, 1
+DUALKV_GATHER, DUALKV_SCATTER = 0, 1
+IMPL_AUTO, IMPL_SCALAR, IMPL_MFMA = 0, 1, 2
+
+_lib = None
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("n_resp", ctypes.c_int32),
+        ("prompt_len", ctypes.c_int32),
+        ("resp_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("impl", ctypes.c_int32),
+        ("resp_valid_len", ctypes.c_void_p),
+    ]
+
+
+def load_library():
+    """Load libdualkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m shared_prompt_exact_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pp = ctypes.POINTER(Params)
+    lib.dualkv_repack.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp]
+    lib.dualkv_repack.restype = ctypes.c_int
+    lib.dualkv_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp]
+    lib.dualkv_fwd.restype = ctypes.c_int
+    lib.dualkv_bwd_workspace_bytes.argtypes = [pp]
+    lib.dualkv_bwd_workspace_bytes.restype = sz
+    lib.dualkv_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dualkv_bwd.restype = ctypes.c_int
+    lib.dualkv_strerror.argtypes = [ctypes.c_int]
+    lib.dualkv_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(code: int, what: str):
+    if code != DUALKV_OK:
+        msg = load_library().dualkv_strerror(code).decode()
+        raise RuntimeError(f"{what}: {msg} (status {code})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DUALKV_F32
+    if t.dtype == torch.bfloat16:
+        return DUALKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, n_resp: int, prompt_len: int, resp_len: int,
+                window: int = 0, softmax_scale: float = 0.0,
+                valid_len: Optional[torch.Tensor] = None, impl: int = IMPL_AUTO) -> Params:
+    T = prompt_len + n_resp * resp_len
+    _require(q, "q")
+    _require(k, "k", dtype=q.dtype)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != T or k.shape[0] != T or q.shape[2] != k.shape[2]:
+        raise ValueError(f"q {tuple(q.shape)} / k {tuple(k.shape)} do not match T = P + N*R = {T}")
+    if valid_len is not None:
+        _require(valid_len, "valid_len", dtype=torch.int32, shape=(n_resp,))
+    return Params(n_resp, prompt_len, resp_len, q.shape[1], k.shape[1], q.shape[2], window,
+                  softmax_scale, _dtype_code(q), impl, None if valid_len is None else valid_len.data_ptr())
+
+
+def dualkv_repack(src: torch.Tensor, n_resp: int, prompt_len: int, resp_len: int, direction: int,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GATHER (replicated -> packed) or SCATTER (packed -> replicated) rows
+    of `src` (first dimension = rows, the rest is the opaque row)."""
+    lib = load_library()
+    _require(src, "src")
+    rows_in = n_resp * (prompt_len + resp_len) if direction == DUALKV_GATHER else prompt_len + n_resp * resp_len
+    rows_out = prompt_len + n_resp * resp_len if direction == DUALKV_GATHER else n_resp * (prompt_len + resp_len)
+    if src.shape[0] != rows_in:
+        raise ValueError(f"src has {src.shape[0]} rows, expected {rows_in}")
+    if out is None:
+        out = torch.empty((rows_out,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    _require(out, "out", dtype=src.dtype, shape=(rows_out,) + tuple(src.shape[1:]))
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else max(1, src.element_size())
+    _check(lib.dualkv_repack(_ptr(src), _ptr(out), row_bytes, n_resp, prompt_len, resp_len,
+                             direction, _stream()), "dualkv_repack")
+    return out
+
+
+def dualkv_fwd(q, k, v, n_resp, prompt_len, resp_len, window=0, softmax_scale=0.0,
+               valid_len=None, impl=IMPL_AUTO, out=None, lse=None):
+    """Forward pass; returns (o [T,Hq,D], lse [Hq,T] fp32)."""
+    lib = load_library()
+    p = make_params(q, k, n_resp, prompt_len, resp_len, window, softmax_scale, valid_len, impl)
+    _require(v, "v", dtype=q.dtype, shape=k.shape)
+    T, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _require(out, "out", dtype=q.dtype, shape=q.shape)
+    _require(lse, "lse", dtype=torch.float32, shape=(Hq, T))
+    _check(lib.dualkv_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream()),
+           "dualkv_fwd")
+    return out, lse
+
+
+def dualkv_bwd_workspace_bytes(q, k, n_resp, prompt_len, resp_len, window=0, softmax_scale=0.0,
+                               valid_len=None, impl=IMPL_AUTO) -> int:
+    p = make_params(q, k, n_resp, prompt_len, resp_len, window, softmax_scale, valid_len, impl)
+    return int(load_library().dualkv_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def dualkv_bwd(q, k, v, o, lse, dout, n_resp, prompt_len, resp_len, window=0, softmax_scale=0.0,
+               valid_len=None, impl=IMPL_AUTO, workspace=None, dq=None, dk=None, dv=None):
+    """Backward pass; returns (dq, dk, dv)."""
+    lib = load_library()
+    p = make_params(q, k, n_resp, prompt_len, resp_len, window, softmax_scale, valid_len, impl)
+    _require(v, "v", dtype=q.dtype, shape=k.shape)
+    _require(o, "o", dtype=q.dtype, shape=q.shape)
+    _require(dout, "dout", dtype=q.dtype, shape=q.shape)
+    _require(lse, "lse", dtype=torch.float32, shape=(q.shape[1], q.shape[0]))
+    need = int(lib.dualkv_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", dtype=torch.uint8)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, name, dtype=ref.dtype, shape=ref.shape)
+    _check(lib.dualkv_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()),
+           "dualkv_bwd")
+    return dq, dk, dv

@@ -1,0 +1,333 @@
+// Forward pass of shared-prompt attention on gfx950 matrix cores.
+//
+// Method: "DualKV: Shared-Prompt Flash Attention for Efficient RL Training
+// with Large Rollouts and Long Contexts" (arXiv 2605.15422), Abstract.  One
+// launch covers every query block of the packed P+NR layout.  A response
+// block walks the shared-prompt key tiles (phase A) and then the key tiles
+// of its own response (phase B) with one running softmax, so the two
+// disjoint key regions merge exactly as in standard attention; a prompt
+// block walks its causal prompt range.
+//
+// Tiling (MI355X-first, not the pages' H100 design):
+//  * a workgroup is NW wave64s; each wave owns 32 query rows of one query
+//    head.  The waves of a workgroup are the query heads of one GQA group
+//    (up to NW of them) times consecutive 32-row slices, so every K/V tile
+//    staged in LDS feeds all of them;
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: each lane then owns one query column, its
+//    row max needs one exchange between wave halves, its row sum none
+//    until the end, and the S^T accumulator becomes the B operand of
+//    O^T += V^T P^T without any data movement;
+//  * Q^T stays in registers for the whole key loop; K tiles sit row-major
+//    in LDS (padded rows, conflict-free 128-bit reads); V tiles are
+//    transposed in registers on their way into LDS, in the perm16 key order
+//    with an XOR chunk swizzle;
+//  * K/V tiles are double buffered: the global loads of tile i+1 are in
+//    flight while tile i is computed, one barrier per tile;
+//  * workgroups are ordered longest key range first and remapped so each
+//    XCD runs a contiguous slice of that order (one KV head's K/V per L2).
+#include "mfma_common.h"
+
+namespace dualkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D, int BN, int NW>
+struct FwdCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int KSTR = D + 8;               // padded K row (elements)
+  static constexpr int K_ELEMS = BN * KSTR;
+  static constexpr int VT_ELEMS = D * BN;
+  static constexpr int STAGE = K_ELEMS + VT_ELEMS;  // elements per buffer
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int KCH = BN * D / 8;            // 16-byte chunks of a K tile
+  static constexpr int KPT = (KCH + NT - 1) / NT;
+  static constexpr int VGR = (BN / 2) * (D / 8);    // (key pair, 8 dims) groups of a V tile
+  static constexpr int VPT = (VGR + NT - 1) / NT;
+};
+
+// Chunk swizzle of the transposed V tile: row d, 16-byte chunk c is stored
+// at chunk c ^ vt_swz(d).  Reads (8 consecutive rows, one chunk) and writes
+// (rows 8 apart) both spread over distinct banks.
+template <int BN>
+__device__ __forceinline__ int vt_swz(int d) {
+  return ((d & 7) ^ ((d >> 3) & 7)) & (BN / 8 - 1);
+}
+
+template <int D, int BN, int NW>
+struct TileStager {
+  using C = FwdCfg<D, BN, NW>;
+  uint4 kr[C::KPT];
+  uint4 vr[C::VPT][2];
+
+  // Load rows [0, nrows) of the K and V tiles starting at packed row `row0`
+  // (KV head `c`); rows >= nrows are zero.
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ k,
+                                       const uint16_t* __restrict__ v, int64_t row0, int nrows,
+                                       int c, int Hkv, int tid) {
+    const int64_t rs = (int64_t)Hkv * D;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int ci = tid + i * C::NT;
+      const int key = ci / (D / 8), c8 = ci % (D / 8);
+      uint4 z = {0, 0, 0, 0};
+      if ((C::KCH % C::NT == 0 || ci < C::KCH) && key < nrows)
+        z = *reinterpret_cast<const uint4*>(k + (row0 + key) * rs + (int64_t)c * D + c8 * 8);
+      kr[i] = z;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int gi = tid + i * C::NT;
+      const int c8 = gi % (D / 8), kp = gi / (D / 8);
+      uint4 z0 = {0, 0, 0, 0}, z1 = {0, 0, 0, 0};
+      if (C::VGR % C::NT == 0 || gi < C::VGR) {
+        const uint16_t* p = v + (row0 + 2 * kp) * rs + (int64_t)c * D + c8 * 8;
+        if (2 * kp < nrows) z0 = *reinterpret_cast<const uint4*>(p);
+        if (2 * kp + 1 < nrows) z1 = *reinterpret_cast<const uint4*>(p + rs);
+      }
+      vr[i][0] = z0;
+      vr[i][1] = z1;
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int ci = tid + i * C::NT;
+      if (C::KCH % C::NT == 0 || ci < C::KCH) {
+        const int key = ci / (D / 8), c8 = ci % (D / 8);
+        *reinterpret_cast<uint4*>(Ks + key * C::KSTR + c8 * 8) = kr[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int gi = tid + i * C::NT;
+      if (C::VGR % C::NT == 0 || gi < C::VGR) {
+        const int c8 = gi % (D / 8), kp = gi / (D / 8);
+        const int pos = perm16(2 * kp);         // keys 2kp, 2kp+1 land side by side
+        const uint32_t x[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+        const uint32_t y[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = c8 * 8 + e;
+          const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(y[e / 2], x[e / 2], 0x07060302u)
+                                     : __builtin_amdgcn_perm(y[e / 2], x[e / 2], 0x05040100u);
+          const int phys = (((pos >> 3) ^ vt_swz<BN>(d)) << 3) | (pos & 7);
+          *reinterpret_cast<uint32_t*>(Vt + d * BN + phys) = w;
+        }
+      }
+    }
+  }
+};
+
+template <int D, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64)
+    fwd_mfma_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
+                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    uint16_t* __restrict__ o, float* __restrict__ lse) {
+  using C = FwdCfg<D, BN, NW>;
+  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BM = 32 * NW / HG;
+  const int NB = nbP + pr.N * nbR;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int hgi = L / NB, blk = L % NB;
+  const int gpw = pr.g / HG;
+  const int c = hgi / gpw;
+  const int h = c * pr.g + (hgi % gpw) * HG + wave % HG;
+  const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
+
+  const int wr0 = b.r0 + (wave / HG) * 32;      // first row of this wave
+  const int my_r = wr0 + l32;
+  const bool qvalid = my_r < b.nvalid;
+  const int qpos = b.posoff + my_r;
+  const int64_t qrow = (int64_t)b.base + my_r;
+  const int64_t ostride = (int64_t)pr.Hq * D;
+
+  const int blk_hi = min(b.r0 + BM, b.nvalid) - 1;   // last valid row of the block
+  const int w_hi = min(wr0 + 31, b.nvalid - 1);
+  const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
+  const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
+
+  // Q^T as B operands, one per 16-wide head-dim step.
+  bf16x8 qB[KT];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk) {
+    uint4 z = {0, 0, 0, 0};
+    if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf);
+    qB[kk] = __builtin_bit_cast(bf16x8, z);
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c2 = pr.scale * kLog2e;
+
+  if (blk_hi >= b.r0) {
+    const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
+    const int ntiles = tr.nA + tr.nB;
+    TileStager<D, BN, NW> st;
+    if (ntiles > 0) {
+      const KeyTile kt = tile_at(pr, b, tr, 0, BN);
+      st.load(k, v, kt.row0, min(BN, kt.lim), c, pr.Hkv, tid);
+      st.store(lds, lds + C::K_ELEMS, tid);
+    }
+    __syncthreads();
+    // Swizzle of the V^T rows this lane reads, one per 32-dim block.
+    int vsw[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vsw[db] = vt_swz<BN>(db * 32 + l32);
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < ntiles) {
+        const KeyTile nx = tile_at(pr, b, tr, it + 1, BN);
+        st.load(k, v, nx.row0, min(BN, nx.lim), c, pr.Hkv, tid);
+      }
+      const KeyTile kt = tile_at(pr, b, tr, it, BN);
+      const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      if (kind != 0) {
+        const uint16_t* Ks = lds + cur * C::STAGE;
+        const uint16_t* Vt = Ks + C::K_ELEMS;
+        f32x16 s[NB32];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * C::KSTR + 16 * kk + 8 * hf);
+            s[kb] = mfma32(a, qB[kk], s[kb]);
+          }
+        if (kind == 2) {
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+              const int kp = kt.pos0 + key;
+              const bool vis = qvalid && key < kt.lim && kp <= qpos && (pr.W <= 0 || qpos - kp < pr.W);
+              if (!vis) s[kb][i] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mnew = fmaxf(m, mx * c2);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - muse);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        bf16x8 pB[K16];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + j], c2, -muse));
+              l += p;
+              pB[2 * kb + hs][j] = (__bf16)p;
+            }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int ks = 0; ks < K16; ++ks) {
+            const int d = db * 32 + l32;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + d * BN + (((2 * ks + hf) ^ vsw[db]) << 3));
+            acc[db] = mfma32(a, pB[ks], acc[db]);
+          }
+      }
+      if (it + 1 < ntiles) st.store(lds + (cur ^ 1) * C::STAGE, lds + (cur ^ 1) * C::STAGE + C::K_ELEMS, tid);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: combine the two halves' partial sums, normalise, write.
+  const float lt = l + swap_halves(l);
+  const bool has = qvalid && lt > 0.f;
+  const float inv = has ? 1.f / lt : 0.f;
+  if (my_r < b.seglen) {
+    uint16_t* orow = o + qrow * ostride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hf;
+        union { __bf16 h[4]; uint2 u; } pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = pk.u;
+      }
+    if (hf == 0)
+      lse[(int64_t)h * pr.T + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+struct FwdPlan {
+  int NW, BN, HG, BM, nbP, nbR;
+  int64_t nwg;
+};
+
+FwdPlan plan(const Problem& pr) {
+  FwdPlan p;
+  p.NW = pr.D <= 128 ? 8 : 4;
+  p.BN = 64;
+  p.HG = heads_per_block(pr.g, p.NW);
+  p.BM = 32 * p.NW / p.HG;
+  p.nbP = (pr.P + p.BM - 1) / p.BM;
+  p.nbR = (pr.R + p.BM - 1) / p.BM;
+  p.nwg = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
+  return p;
+}
+
+template <int D, int BN, int NW>
+hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k, const void* v,
+               void* o, float* lse, hipStream_t stream) {
+  using C = FwdCfg<D, BN, NW>;
+  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW>, C::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  return launch(fwd_mfma_kernel<D, BN, NW>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
+                stream, pr, p.HG, p.nbP, p.nbR, static_cast<const uint16_t*>(q),
+                static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                static_cast<uint16_t*>(o), lse);
+}
+
+}  // namespace
+
+bool fwd_mfma_supported(const Problem& pr) {
+  if (pr.D != 64 && pr.D != 128 && pr.D != 256) return false;
+  const FwdPlan p = plan(pr);
+  return p.nwg < ((int64_t)1 << 31);
+}
+
+hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, const void* v, void* o,
+                           float* lse, hipStream_t stream) {
+  const FwdPlan p = plan(pr);
+  if (p.nwg == 0) return hipSuccess;
+  switch (pr.D) {
+    case 64: return run<64, 64, 8>(pr, p, q, k, v, o, lse, stream);
+    case 128: return run<128, 64, 8>(pr, p, q, k, v, o, lse, stream);
+    case 256: return run<256, 64, 4>(pr, p, q, k, v, o, lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dualkv

@@ -1,0 +1,90 @@
+// Shared device/host definitions for the shared-prompt attention kernels
+// (gfx950 only).  The packed layout, positions, masks and GQA mapping are
+// those documented in include/dualkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dualkv.h"
+
+namespace dualkv {
+
+// Validated problem description passed by value to every kernel.
+struct Problem {
+  int N, P, R;          // responses, prompt length, padded response length
+  int Hq, Hkv, D;       // heads and head dim
+  int g;                // Hq / Hkv
+  int W;                // window (<= 0: none)
+  int T;                // P + N*R packed rows
+  float scale;          // softmax scale (> 0)
+  const int32_t* valid_len;  // device [N] or nullptr
+};
+
+__device__ __forceinline__ int resp_valid(const Problem& pr, int n) {
+  if (pr.valid_len == nullptr) return pr.R;
+  int L = pr.valid_len[n];
+  return L < 0 ? 0 : (L > pr.R ? pr.R : L);
+}
+
+// bf16 <-> fp32 on raw 16-bit patterns (round to nearest even; inputs of
+// these kernels are finite, NaN is kept quiet).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Launch a kernel and return the runtime's status for that launch (the
+// status of hipLaunchKernel itself, not a stale error of an earlier call).
+template <typename... KArgs, typename... Args>
+static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                                hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  auto go = [&](KArgs... conv) -> hipError_t {
+    void* ptrs[] = {static_cast<void*>(&conv)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, stream);
+  };
+  return go(static_cast<KArgs>(args)...);
+}
+
+// ---- launchers implemented in the kernel translation units -------------
+hipError_t launch_repack(const void* src, void* dst, int64_t row_bytes, int N, int P, int R,
+                         int direction, hipStream_t stream);
+
+hipError_t launch_fwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
+                             const void* v, void* o, float* lse, hipStream_t stream);
+hipError_t launch_bwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+
+bool fwd_mfma_supported(const Problem& pr);
+hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
+                           void* o, float* lse, hipStream_t stream);
+
+bool bwd_mfma_supported(const Problem& pr);
+size_t bwd_mfma_workspace_bytes(const Problem& pr);
+hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, void* workspace, hipStream_t stream);
+
+// Shared by the scalar backward and the MFMA backward: delta[h][t] =
+// sum_d dO[t,h,d] * O[t,h,d] in fp32 (0 on rows with no visible key).
+hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const void* dout,
+                            const float* lse, float* delta, hipStream_t stream);
+
+}  // namespace dualkv

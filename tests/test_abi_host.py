@@ -1,0 +1,102 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function declared in
+include/dualkv.h, and reject invalid arguments on the host before any HIP
+call, with the documented status codes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import shared_prompt_exact_amd as dk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dualkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dk.LIB_PATH), reason="libdualkv.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dualkv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = dk.load_library()
+    names = declared_functions()
+    assert set(names) >= {"dualkv_repack", "dualkv_fwd", "dualkv_bwd",
+                          "dualkv_bwd_workspace_bytes", "dualkv_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def params(**kw):
+    base = dict(n_resp=4, prompt_len=64, resp_len=32, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                window=0, softmax_scale=0.0, dtype=dk.DUALKV_BF16, impl=0, resp_valid_len=None)
+    base.update(kw)
+    return dk.Params(**base)
+
+
+def fwd_status(p):
+    dummy = ctypes.c_void_p(0x1000)
+    return dk.load_library().dualkv_fwd(ctypes.byref(p) if p is not None else None,
+                                        dummy, dummy, dummy, dummy, dummy, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_resp=0), 1), (dict(prompt_len=-1), 1), (dict(resp_len=-2), 1),
+    (dict(n_q_heads=6, n_kv_heads=4), 1), (dict(n_kv_heads=0), 1), (dict(head_dim=0), 1),
+    (dict(head_dim=513), 2), (dict(dtype=7), 1), (dict(impl=9), 1),
+    (dict(softmax_scale=-1.0), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(dtype=dk.DUALKV_F32, impl=dk.IMPL_MFMA), 2),
+    (dict(head_dim=96, impl=dk.IMPL_MFMA), 2),
+])
+def test_invalid_parameters_rejected(kw, code):
+    assert fwd_status(params(**kw)) == code
+
+
+def test_null_params_and_pointers():
+    lib = dk.load_library()
+    assert fwd_status(None) == 1
+    p = params()
+    assert lib.dualkv_fwd(ctypes.byref(p), None, None, None, None, None, None) == 1
+    assert lib.dualkv_bwd_workspace_bytes(None) == 0
+    assert lib.dualkv_bwd_workspace_bytes(ctypes.byref(params(n_resp=0))) == 0
+
+
+def test_empty_problem_is_a_no_op():
+    # P = R = 0: nothing to compute, success without touching the device
+    p = params(prompt_len=0, resp_len=0)
+    lib = dk.load_library()
+    assert lib.dualkv_fwd(ctypes.byref(p), None, None, None, None, None, None) == 0
+
+
+def test_workspace_too_small():
+    lib = dk.load_library()
+    p = params()
+    need = lib.dualkv_bwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0 and need % 256 == 0
+    d = ctypes.c_void_p(0x1000)
+    st = lib.dualkv_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, need - 1, None)
+    assert st == 3
+
+
+def test_repack_argument_checks():
+    lib = dk.load_library()
+    d = ctypes.c_void_p(0x1000)
+    assert lib.dualkv_repack(d, d, 0, 2, 3, 4, 0, None) == 1       # row_bytes < 1
+    assert lib.dualkv_repack(d, d, 16, 0, 3, 4, 0, None) == 1      # N < 1
+    assert lib.dualkv_repack(d, d, 16, 2, -1, 4, 0, None) == 1     # P < 0
+    assert lib.dualkv_repack(d, d, 16, 2, 3, 4, 5, None) == 1      # direction
+    assert lib.dualkv_repack(None, d, 16, 2, 3, 4, 0, None) == 1   # null with rows
+    assert lib.dualkv_repack(None, None, 16, 2, 0, 0, 0, None) == 0  # nothing to copy
+
+
+def test_strerror():
+    lib = dk.load_library()
+    assert lib.dualkv_strerror(0) == b"success"
+    assert lib.dualkv_strerror(3) == b"workspace too small"
+    assert lib.dualkv_strerror(99) == b"unknown status"
