@@ -1,14 +1,649 @@
-// Backward pass on gfx950 matrix cores (not yet built: the scalar path
-// serves every backward until this lands).
-#include "mfma_common.h"
+// Backward pass of shared-prompt attention on gfx950 matrix cores.
+//
+// Method: "DualKV: Shared-Prompt Flash Attention for Efficient RL Training
+// with Large Rollouts and Long Contexts" (arXiv 2605.15422), Abstract: the
+// backward iterates over the same two disjoint key regions as the forward,
+// and the gradient of a shared-prompt key or value is the sum of the
+// contributions of the prompt's own queries and of every response.
+//
+// Per visible (query i, key j) pair of a head, with p = exp(scale*q.k - LSE_i)
+// and Delta_i = dO_i . O_i:
+//   dV_j += p dO_i,   dp = dO_i . v_j,   ds = p (dp - Delta_i),
+//   dK_j += scale ds q_i,   dQ_i += scale ds k_j.
+//
+// Three kernels, all deterministic (no atomics; every sum has a fixed order):
+//  1. delta  : Delta = rowsum(dO * O) (HBM bound, shared with the scalar path);
+//  2. dq     : query-parallel, the forward's tiling (K, V row-major and K^T
+//              in LDS, Q^T and dO^T in registers); recomputes S and dP;
+//  3. dkdv   : key-parallel.  A workgroup owns 32*NWK keys of one KV head
+//              (32 per wave, K and V held as B operands in registers) and
+//              streams 32-row query stages (Q, dO row-major and transposed
+//              in LDS) of every query head of the group.  A prompt key tile
+//              is split into slots: slot 0 takes the prompt's own queries,
+//              slots 1.. take fixed ranges of responses.  With more than one
+//              slot each writes fp32 partial dK/dV and
+//  4. reduce : sums the slots of every prompt row in ascending slot order.
+// The prompt K/V tile is thereby reused by the query blocks of all N
+// responses inside one workgroup, and the N-fold sum never leaves a fixed
+// order, so results are bitwise reproducible.
+#include "tiles.h"
 
 namespace dualkv {
+namespace {
 
-bool bwd_mfma_supported(const Problem&) { return false; }
-size_t bwd_mfma_workspace_bytes(const Problem&) { return 0; }
-hipError_t launch_bwd_mfma(const Problem&, const void*, const void*, const void*, const void*,
-                           const float*, const void*, void*, void*, void*, void*, hipStream_t) {
-  return hipErrorInvalidValue;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------------- dq kernel
+
+template <int D, int BN, int NW>
+struct DqCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int KSTR = D + 8;
+  static constexpr int K_ELEMS = BN * KSTR;      // K row-major
+  static constexpr int V_ELEMS = BN * KSTR;      // V row-major
+  static constexpr int KT_ELEMS = D * BN;        // K transposed
+  static constexpr int STAGE = K_ELEMS + V_ELEMS + KT_ELEMS;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+};
+
+template <int D, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64)
+    bwd_dq_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
+                  const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                  const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                  const float* __restrict__ delta, uint16_t* __restrict__ dq) {
+  using C = DqCfg<D, BN, NW>;
+  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BM = 32 * NW / HG;
+  const int NB = nbP + pr.N * nbR;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int hgi = L / NB, blk = L % NB;
+  const int gpw = pr.g / HG;
+  const int c = hgi / gpw;
+  const int h = c * pr.g + (hgi % gpw) * HG + wave % HG;
+  const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
+
+  const int wr0 = b.r0 + (wave / HG) * 32;
+  const int my_r = wr0 + l32;
+  const bool qvalid = my_r < b.nvalid;
+  const int qpos = b.posoff + my_r;
+  const int64_t qrow = (int64_t)b.base + my_r;
+  const int64_t ostride = (int64_t)pr.Hq * D;
+  const int blk_hi = min(b.r0 + BM, b.nvalid) - 1;
+  const int w_hi = min(wr0 + 31, b.nvalid - 1);
+  const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
+  const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
+
+  bf16x8 qB[KT], doB[KT];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk) {
+    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (qvalid) {
+      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf;
+      z = *reinterpret_cast<const uint4*>(q + off);
+      y = *reinterpret_cast<const uint4*>(dout + off);
+    }
+    qB[kk] = __builtin_bit_cast(bf16x8, z);
+    doB[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  float lse2 = INFINITY, dlt = 0.f;   // +inf: p = 0 for rows without keys
+  if (qvalid) {
+    const float Lr = lse[(int64_t)h * pr.T + qrow];
+    lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
+    dlt = delta[(int64_t)h * pr.T + qrow];
+  }
+  const float c2 = pr.scale * kLog2e;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  if (blk_hi >= b.r0) {
+    const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
+    const int ntiles = tr.nA + tr.nB;
+    const int64_t rs = (int64_t)pr.Hkv * D;
+    PairTile<BN, D, C::NT> kst, vst;
+    if (ntiles > 0) {
+      const KeyTile kt = tile_at(pr, b, tr, 0, BN);
+      const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
+      kst.load(k + off, rs, min(BN, kt.lim), tid);
+      vst.load(v + off, rs, min(BN, kt.lim), tid);
+      kst.store_rows(lds, tid);
+      vst.store_rows(lds + C::K_ELEMS, tid);
+      kst.store_trans(lds + C::K_ELEMS + C::V_ELEMS, tid);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      if (it + 1 < ntiles) {
+        const KeyTile nx = tile_at(pr, b, tr, it + 1, BN);
+        const int64_t off = (int64_t)nx.row0 * rs + (int64_t)c * D;
+        kst.load(k + off, rs, min(BN, nx.lim), tid);
+        vst.load(v + off, rs, min(BN, nx.lim), tid);
+      }
+      const KeyTile kt = tile_at(pr, b, tr, it, BN);
+      const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      if (kind != 0) {
+        const uint16_t* Ks = lds + cur * C::STAGE;
+        const uint16_t* Vs = Ks + C::K_ELEMS;
+        const uint16_t* Kt = Vs + C::V_ELEMS;
+        f32x16 s[NB32], dp[NB32];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb) {
+            const int ro = (kb * 32 + l32) * C::KSTR + 16 * kk + 8 * hf;
+            s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + ro), qB[kk], s[kb]);
+            dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + ro), doB[kk], dp[kb]);
+          }
+        bf16x8 dsB[K16];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * hs + j;
+              float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
+              if (kind == 2) {
+                const int key = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                const int kp = kt.pos0 + key;
+                const bool vis = qvalid && key < kt.lim && kp <= qpos && (pr.W <= 0 || qpos - kp < pr.W);
+                if (!vis) p = 0.f;
+              }
+              dsB[2 * kb + hs][j] = (__bf16)(p * (dp[kb][i] - dlt));
+            }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int ks = 0; ks < K16; ++ks)
+            acc[db] = mfma32(trans_read<BN>(Kt, db * 32 + l32, ks, hf), dsB[ks], acc[db]);
+      }
+      if (it + 1 < ntiles) {
+        uint16_t* nb = lds + (cur ^ 1) * C::STAGE;
+        kst.store_rows(nb, tid);
+        vst.store_rows(nb + C::K_ELEMS, tid);
+        kst.store_trans(nb + C::K_ELEMS + C::V_ELEMS, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  if (my_r < b.seglen) {
+    uint16_t* orow = dq + qrow * ostride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        union { __bf16 h[4]; uint2 u; } pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
+        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g4 + 4 * hf) = pk.u;
+      }
+  }
+}
+
+// --------------------------------------------------------------- dkdv kernel
+
+constexpr int kStageRows = 32;
+
+template <int D, int NWK>
+struct KvCfg {
+  static constexpr int NT = NWK * 64;
+  static constexpr int BK = 32 * NWK;            // keys per workgroup
+  static constexpr int QSTR = D + 8;
+  static constexpr int Q_ELEMS = kStageRows * QSTR;   // Q rows
+  static constexpr int DO_ELEMS = kStageRows * QSTR;  // dO rows
+  static constexpr int QT_ELEMS = D * kStageRows;     // Q^T
+  static constexpr int DOT_ELEMS = D * kStageRows;    // dO^T
+  static constexpr int STAT = 2 * kStageRows * 2;     // lse2, delta (fp32 as 2 x u16)
+  static constexpr int STAGE = Q_ELEMS + DO_ELEMS + QT_ELEMS + DOT_ELEMS + STAT;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+};
+
+// Work item of the dK/dV kernel.
+struct KvItem {
+  int c;          // KV head
+  int seg;        // -1: prompt key tile; else response n
+  int k0;         // first key row inside its segment
+  int slot;       // prompt tiles: slot (0 = prompt queries, s >= 1 = responses)
+};
+
+// Query segments visited by an item and their row ranges.
+struct QueryPlan {
+  int first, last;   // segment ids (-1 = prompt) in ascending order
+};
+
+// Walks (segment, 32-row stage, query head) in a fixed order.
+struct StageIter {
+  int seg, seg_last;
+  int r, r_end;       // current stage row and the segment's row bound
+  int h, h0, h1;
+  bool ok;
+};
+
+struct KvShape {
+  int slots;          // slots per prompt tile
+  int per_slot;       // responses per slot (slots >= 2)
+  int nPt, nRt;       // prompt / response key tiles per KV head
+};
+
+// Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
+// positions) of the item; lo is rounded down to a stage boundary.
+__device__ __forceinline__ void seg_rows(const Problem& pr, int seg, int kp_lo, int kp_hi, int& lo,
+                                         int& hi) {
+  if (seg < 0) {
+    lo = (kp_lo / kStageRows) * kStageRows;
+    hi = pr.W > 0 ? min(pr.P, kp_hi + pr.W) : pr.P;
+  } else {
+    const int Lv = resp_valid(pr, seg);
+    const int rlo = max(0, kp_lo - pr.P);
+    lo = (rlo / kStageRows) * kStageRows;
+    hi = Lv;
+    if (pr.W > 0) hi = min(hi, max(0, kp_hi + pr.W - pr.P));
+  }
+}
+
+__device__ __forceinline__ void iter_fix(const Problem& pr, StageIter& s, int kp_lo, int kp_hi) {
+  // move to the first non-empty segment at or after s.seg
+  while (s.seg <= s.seg_last) {
+    int lo, hi;
+    seg_rows(pr, s.seg, kp_lo, kp_hi, lo, hi);
+    if (s.r < lo) s.r = lo;
+    if (s.r < hi) {
+      s.r_end = hi;
+      s.ok = true;
+      return;
+    }
+    ++s.seg;
+    s.r = 0;
+  }
+  s.ok = false;
+}
+
+__device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int kp_lo, int kp_hi) {
+  if (++s.h < s.h1) return;
+  s.h = s.h0;
+  s.r += kStageRows;
+  if (s.r < s.r_end) return;
+  ++s.seg;
+  s.r = 0;
+  iter_fix(pr, s, kp_lo, kp_hi);
+}
+
+template <int D, int NWK>
+__global__ void __launch_bounds__(NWK * 64)
+    bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
+                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                    const float* __restrict__ delta, uint16_t* __restrict__ dk,
+                    uint16_t* __restrict__ dv, float* __restrict__ part_k,
+                    float* __restrict__ part_v) {
+  using C = KvCfg<D, NWK>;
+  constexpr int KT = D / 16, DB = D / 32;
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- decode the work item (longest first, one KV head per XCD slice)
+  const int per_head = sh.nPt * sh.slots + pr.N * sh.nRt;
+  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
+  KvItem it;
+  it.c = Lid / per_head;
+  int x = Lid % per_head;
+  if (x < sh.nPt * sh.slots) {
+    it.seg = -1;
+    if (sh.slots > 1 && x < sh.nPt * (sh.slots - 1)) {   // response slots first
+      it.slot = 1 + x / sh.nPt;
+      it.k0 = (x % sh.nPt) * C::BK;
+    } else {                                              // then the prompt slot
+      it.slot = 0;
+      it.k0 = (x - sh.nPt * (sh.slots - 1)) * C::BK;
+    }
+  } else {
+    x -= sh.nPt * sh.slots;
+    it.seg = x % pr.N;
+    it.k0 = (x / pr.N) * C::BK;
+    it.slot = 0;
+  }
+  const int c = it.c;
+  const int seg_base = it.seg < 0 ? 0 : pr.P + it.seg * pr.R;
+  const int seg_valid = it.seg < 0 ? pr.P : resp_valid(pr, it.seg);
+  const int seg_len = it.seg < 0 ? pr.P : pr.R;
+  const int posoff = it.seg < 0 ? 0 : pr.P;
+  const int klim = seg_valid - it.k0;                 // valid keys of the tile
+  const int kp_lo = posoff + it.k0;
+  const int kp_hi = posoff + it.k0 + min(C::BK, max(klim, 1)) - 1;
+
+  // ---- this wave's 32 keys as B operands (K^T and V^T slices)
+  const int wk0 = 32 * wave;                          // first key of the wave in the tile
+  const int my_k = wk0 + l32;
+  const bool kvalid = my_k < klim;
+  const int kpos = kp_lo + my_k;
+  const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
+  const int64_t kstride = (int64_t)pr.Hkv * D;
+  bf16x8 kB[KT], vB[KT];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk) {
+    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (kvalid) {
+      const int64_t off = krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf;
+      z = *reinterpret_cast<const uint4*>(k + off);
+      y = *reinterpret_cast<const uint4*>(v + off);
+    }
+    kB[kk] = __builtin_bit_cast(bf16x8, z);
+    vB[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
+  const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
+
+  f32x16 dKt[DB], dVt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dKt[db][i] = dVt[db][i] = 0.f;
+
+  // ---- the query stages of this item
+  StageIter cur;
+  if (it.seg >= 0) {
+    cur.seg = cur.seg_last = it.seg;
+  } else if (it.slot == 0) {
+    cur.seg = cur.seg_last = -1;
+  } else {
+    cur.seg = (it.slot - 1) * sh.per_slot;
+    cur.seg_last = min(pr.N, it.slot * sh.per_slot) - 1;
+  }
+  cur.h0 = cur.h = c * pr.g;
+  cur.h1 = (c + 1) * pr.g;
+  cur.r = 0;
+  cur.ok = false;
+  if (klim > 0) iter_fix(pr, cur, kp_lo, kp_hi);
+  StageIter nxt = cur;
+  if (nxt.ok) iter_next(pr, nxt, kp_lo, kp_hi);
+
+  const int64_t qstride = (int64_t)pr.Hq * D;
+  const float c2 = pr.scale * kLog2e;
+  PairTile<kStageRows, D, C::NT> qst, dost;
+  float st_l = INFINITY, st_d = 0.f;     // per-thread stage statistics (threads < 32)
+
+  auto stage_load = [&](const StageIter& s) {
+    const int sb = s.seg < 0 ? 0 : pr.P + s.seg * pr.R;
+    const int svalid = s.seg < 0 ? pr.P : resp_valid(pr, s.seg);
+    const int n = min(kStageRows, svalid - s.r);
+    const int64_t off = ((int64_t)sb + s.r) * qstride + (int64_t)s.h * D;
+    qst.load(q + off, qstride, n, tid);
+    dost.load(dout + off, qstride, n, tid);
+    if (tid < kStageRows) {
+      st_l = INFINITY;
+      st_d = 0.f;
+      if (tid < n) {
+        const int64_t idx = (int64_t)s.h * pr.T + sb + s.r + tid;
+        const float Lr = lse[idx];
+        st_l = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
+        st_d = delta[idx];
+      }
+    }
+  };
+  auto stage_store = [&](uint16_t* buf) {
+    qst.store_rows(buf, tid);
+    dost.store_rows(buf + C::Q_ELEMS, tid);
+    qst.store_trans(buf + C::Q_ELEMS + C::DO_ELEMS, tid);
+    dost.store_trans(buf + C::Q_ELEMS + C::DO_ELEMS + C::QT_ELEMS, tid);
+    float* stat = reinterpret_cast<float*>(buf + C::Q_ELEMS + C::DO_ELEMS + C::QT_ELEMS + C::DOT_ELEMS);
+    if (tid < kStageRows) {
+      stat[tid] = st_l;
+      stat[kStageRows + tid] = st_d;
+    }
+  };
+
+  int buf = 0;
+  if (cur.ok) {
+    stage_load(cur);
+    stage_store(lds);
+  }
+  __syncthreads();
+  while (cur.ok) {
+    if (nxt.ok) stage_load(nxt);
+    // ---- compute on stage `cur`
+    {
+      const uint16_t* Qs = lds + buf * C::STAGE;
+      const uint16_t* DOs = Qs + C::Q_ELEMS;
+      const uint16_t* QT = DOs + C::DO_ELEMS;
+      const uint16_t* DOT = QT + C::QT_ELEMS;
+      const float* stat = reinterpret_cast<const float*>(DOT + C::DOT_ELEMS);
+      const int svalid = cur.seg < 0 ? pr.P : resp_valid(pr, cur.seg);
+      const int s_posoff = cur.seg < 0 ? 0 : pr.P;
+      const int nrows = min(kStageRows, svalid - cur.r);
+      const int sq_lo = s_posoff + cur.r, sq_hi = sq_lo + nrows - 1;
+      // skip / full / masked for this wave's keys against the stage's queries
+      int kind;
+      if (wk_valid <= 0 || nrows <= 0 || sq_hi < wkp_lo || (pr.W > 0 && sq_lo - wkp_hi >= pr.W)) kind = 0;
+      else if (wk_valid == 32 && nrows == kStageRows && sq_lo >= wkp_hi &&
+               (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
+      else kind = 2;
+      if (kind != 0) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+          const int ro = l32 * C::QSTR + 16 * kk + 8 * hf;
+          s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ro), kB[kk], s);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(DOs + ro), vB[kk], dp);
+        }
+        bf16x8 pB[2], dsB[2];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * g4 + 4 * hf);
+          const float4 d4 = *reinterpret_cast<const float4*>(stat + kStageRows + 8 * g4 + 4 * hf);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;                       // register index
+            const int qi = 8 * g4 + 4 * hf + e;             // query row in the stage
+            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
+            if (kind == 2) {
+              const int qp = sq_lo + qi;
+              const bool vis = kvalid && qi < nrows && kpos <= qp && (pr.W <= 0 || qp - kpos < pr.W);
+              if (!vis) p = 0.f;
+            }
+            const float ds = p * (dp[i] - dv4[e]);
+            pB[i >> 3][i & 7] = (__bf16)p;
+            dsB[i >> 3][i & 7] = (__bf16)ds;
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            dVt[db] = mfma32(trans_read<kStageRows>(DOT, db * 32 + l32, ks, hf), pB[ks], dVt[db]);
+            dKt[db] = mfma32(trans_read<kStageRows>(QT, db * 32 + l32, ks, hf), dsB[ks], dKt[db]);
+          }
+      }
+    }
+    if (nxt.ok) stage_store(lds + (buf ^ 1) * C::STAGE);
+    __syncthreads();
+    cur = nxt;
+    if (nxt.ok) iter_next(pr, nxt, kp_lo, kp_hi);
+    buf ^= 1;
+  }
+
+  // ---- write dK (scaled) and dV for this lane's key
+  if (my_k < seg_len - it.k0 && it.k0 + my_k < seg_len) {
+    const bool partial = it.seg < 0 && sh.slots > 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hf;
+        if (partial) {
+          const int64_t o = (((int64_t)it.slot * pr.P + it.k0 + my_k) * pr.Hkv + c) * D + d;
+          *reinterpret_cast<float4*>(part_k + o) =
+              make_float4(dKt[db][4 * g4] * pr.scale, dKt[db][4 * g4 + 1] * pr.scale,
+                          dKt[db][4 * g4 + 2] * pr.scale, dKt[db][4 * g4 + 3] * pr.scale);
+          *reinterpret_cast<float4*>(part_v + o) =
+              make_float4(dVt[db][4 * g4], dVt[db][4 * g4 + 1], dVt[db][4 * g4 + 2], dVt[db][4 * g4 + 3]);
+        } else {
+          const int64_t o = krow * kstride + (int64_t)c * D + d;
+          union { __bf16 h[4]; uint2 u; } pk, pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk.h[e] = (__bf16)(dKt[db][4 * g4 + e] * pr.scale);
+            pv.h[e] = (__bf16)dVt[db][4 * g4 + e];
+          }
+          *reinterpret_cast<uint2*>(dk + o) = pk.u;
+          *reinterpret_cast<uint2*>(dv + o) = pv.u;
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------ slot reduction
+
+__global__ void __launch_bounds__(256)
+    reduce_slots_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v,
+                        int slots, int64_t n4, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = reinterpret_cast<const float4*>(part_k)[i];
+    float4 b = reinterpret_cast<const float4*>(part_v)[i];
+    for (int s = 1; s < slots; ++s) {     // ascending slot order
+      const float4 x = reinterpret_cast<const float4*>(part_k)[s * n4 + i];
+      const float4 y = reinterpret_cast<const float4*>(part_v)[s * n4 + i];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+    union { __bf16 h[4]; uint2 u; } pk, pv;
+    pk.h[0] = (__bf16)a.x; pk.h[1] = (__bf16)a.y; pk.h[2] = (__bf16)a.z; pk.h[3] = (__bf16)a.w;
+    pv.h[0] = (__bf16)b.x; pv.h[1] = (__bf16)b.y; pv.h[2] = (__bf16)b.z; pv.h[3] = (__bf16)b.w;
+    reinterpret_cast<uint2*>(dk)[i] = pk.u;
+    reinterpret_cast<uint2*>(dv)[i] = pv.u;
+  }
+}
+
+// ------------------------------------------------------------------ planning
+
+constexpr int kDqBN = 64;
+constexpr int kNWK = 4;
+
+struct BwdPlan {
+  int NW, HG, BM, nbP, nbR;
+  int64_t nwg_dq;
+  KvShape sh;
+  int64_t nwg_kv;
+  size_t off_delta, off_pk, off_pv, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdPlan plan(const Problem& pr) {
+  BwdPlan p;
+  p.NW = pr.D <= 64 ? 8 : 4;
+  p.HG = heads_per_block(pr.g, p.NW);
+  p.BM = 32 * p.NW / p.HG;
+  p.nbP = (pr.P + p.BM - 1) / p.BM;
+  p.nbR = (pr.R + p.BM - 1) / p.BM;
+  p.nwg_dq = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
+  const int BK = 32 * kNWK;
+  p.sh.nPt = (pr.P + BK - 1) / BK;
+  p.sh.nRt = (pr.R + BK - 1) / BK;
+  // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
+  // most P of them); the responses are cut into ranges of about P queries
+  // each, so no slot is much longer than the longest prompt slot.
+  int rslots = 0;
+  if (pr.P > 0 && pr.R > 0) {
+    const int64_t nr = (int64_t)pr.N * pr.R;
+    rslots = (int)((nr + pr.P - 1) / pr.P);
+    rslots = max(1, min(rslots, pr.N));
+  }
+  p.sh.per_slot = rslots > 0 ? (pr.N + rslots - 1) / rslots : 1;
+  if (rslots > 0) rslots = (pr.N + p.sh.per_slot - 1) / p.sh.per_slot;
+  p.sh.slots = 1 + rslots;
+  p.nwg_kv = ((int64_t)p.sh.nPt * p.sh.slots + (int64_t)pr.N * p.sh.nRt) * pr.Hkv;
+  p.off_delta = 0;
+  size_t b = align256((size_t)pr.Hq * pr.T * sizeof(float));
+  p.off_pk = b;
+  const size_t part = p.sh.slots > 1 ? align256((size_t)p.sh.slots * pr.P * pr.Hkv * pr.D * sizeof(float)) : 0;
+  p.off_pv = p.off_pk + part;
+  p.bytes = p.off_pv + part;
+  return p;
+}
+
+template <int D, int NW, int NWK>
+hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, char* ws,
+               hipStream_t stream) {
+  using CQ = DqCfg<D, kDqBN, NW>;
+  using CK = KvCfg<D, NWK>;
+  static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW>, CQ::LDS_BYTES);
+  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK>, CK::LDS_BYTES);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+  const float* delta = reinterpret_cast<const float*>(ws + p.off_delta);
+  float* pk = reinterpret_cast<float*>(ws + p.off_pk);
+  float* pv = reinterpret_cast<float*>(ws + p.off_pv);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const uint16_t* do16 = static_cast<const uint16_t*>(dout);
+  hipError_t e;
+  if (p.nwg_dq > 0) {
+    e = launch(bwd_dq_kernel<D, kDqBN, NW>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
+               stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
+               static_cast<uint16_t*>(dq));
+    if (e != hipSuccess) return e;
+  }
+  if (p.nwg_kv > 0) {
+    e = launch(bwd_dkdv_kernel<D, NWK>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
+               stream, pr, p.sh, q16, k16, v16, do16, lse, delta, static_cast<uint16_t*>(dk),
+               static_cast<uint16_t*>(dv), pk, pv);
+    if (e != hipSuccess) return e;
+  }
+  if (p.sh.slots > 1 && pr.P > 0) {
+    const int64_t n4 = (int64_t)pr.P * pr.Hkv * D / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    e = launch(reduce_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pk, pv,
+               p.sh.slots, n4, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const Problem& pr) {
+  if (pr.D != 64 && pr.D != 128) return false;
+  const BwdPlan p = plan(pr);
+  return p.nwg_dq < ((int64_t)1 << 31) && p.nwg_kv < ((int64_t)1 << 31);
+}
+
+size_t bwd_mfma_workspace_bytes(const Problem& pr) { return plan(pr).bytes; }
+
+hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, void* workspace, hipStream_t stream) {
+  const BwdPlan p = plan(pr);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = launch_bwd_delta(pr, DUALKV_BF16, o, dout, lse,
+                                  reinterpret_cast<float*>(ws + p.off_delta), stream);
+  if (e != hipSuccess) return e;
+  switch (pr.D) {
+    case 64: return run<64, 8, kNWK>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 4, kNWK>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dualkv

@@ -26,7 +26,7 @@
 //    flight while tile i is computed, one barrier per tile;
 //  * workgroups are ordered longest key range first and remapped so each
 //    XCD runs a contiguous slice of that order (one KV head's K/V per L2).
-#include "mfma_common.h"
+#include "tiles.h"
 
 namespace dualkv {
 namespace {
@@ -42,84 +42,6 @@ struct FwdCfg {
   static constexpr int VT_ELEMS = D * BN;
   static constexpr int STAGE = K_ELEMS + VT_ELEMS;  // elements per buffer
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int KCH = BN * D / 8;            // 16-byte chunks of a K tile
-  static constexpr int KPT = (KCH + NT - 1) / NT;
-  static constexpr int VGR = (BN / 2) * (D / 8);    // (key pair, 8 dims) groups of a V tile
-  static constexpr int VPT = (VGR + NT - 1) / NT;
-};
-
-// Chunk swizzle of the transposed V tile: row d, 16-byte chunk c is stored
-// at chunk c ^ vt_swz(d).  Reads (8 consecutive rows, one chunk) and writes
-// (rows 8 apart) both spread over distinct banks.
-template <int BN>
-__device__ __forceinline__ int vt_swz(int d) {
-  return ((d & 7) ^ ((d >> 3) & 7)) & (BN / 8 - 1);
-}
-
-template <int D, int BN, int NW>
-struct TileStager {
-  using C = FwdCfg<D, BN, NW>;
-  uint4 kr[C::KPT];
-  uint4 vr[C::VPT][2];
-
-  // Load rows [0, nrows) of the K and V tiles starting at packed row `row0`
-  // (KV head `c`); rows >= nrows are zero.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ k,
-                                       const uint16_t* __restrict__ v, int64_t row0, int nrows,
-                                       int c, int Hkv, int tid) {
-    const int64_t rs = (int64_t)Hkv * D;
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int ci = tid + i * C::NT;
-      const int key = ci / (D / 8), c8 = ci % (D / 8);
-      uint4 z = {0, 0, 0, 0};
-      if ((C::KCH % C::NT == 0 || ci < C::KCH) && key < nrows)
-        z = *reinterpret_cast<const uint4*>(k + (row0 + key) * rs + (int64_t)c * D + c8 * 8);
-      kr[i] = z;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
-      const int gi = tid + i * C::NT;
-      const int c8 = gi % (D / 8), kp = gi / (D / 8);
-      uint4 z0 = {0, 0, 0, 0}, z1 = {0, 0, 0, 0};
-      if (C::VGR % C::NT == 0 || gi < C::VGR) {
-        const uint16_t* p = v + (row0 + 2 * kp) * rs + (int64_t)c * D + c8 * 8;
-        if (2 * kp < nrows) z0 = *reinterpret_cast<const uint4*>(p);
-        if (2 * kp + 1 < nrows) z1 = *reinterpret_cast<const uint4*>(p + rs);
-      }
-      vr[i][0] = z0;
-      vr[i][1] = z1;
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vt, int tid) const {
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int ci = tid + i * C::NT;
-      if (C::KCH % C::NT == 0 || ci < C::KCH) {
-        const int key = ci / (D / 8), c8 = ci % (D / 8);
-        *reinterpret_cast<uint4*>(Ks + key * C::KSTR + c8 * 8) = kr[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
-      const int gi = tid + i * C::NT;
-      if (C::VGR % C::NT == 0 || gi < C::VGR) {
-        const int c8 = gi % (D / 8), kp = gi / (D / 8);
-        const int pos = perm16(2 * kp);         // keys 2kp, 2kp+1 land side by side
-        const uint32_t x[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-        const uint32_t y[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = c8 * 8 + e;
-          const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(y[e / 2], x[e / 2], 0x07060302u)
-                                     : __builtin_amdgcn_perm(y[e / 2], x[e / 2], 0x05040100u);
-          const int phys = (((pos >> 3) ^ vt_swz<BN>(d)) << 3) | (pos & 7);
-          *reinterpret_cast<uint32_t*>(Vt + d * BN + phys) = w;
-        }
-      }
-    }
-  }
 };
 
 template <int D, int BN, int NW>
@@ -174,23 +96,25 @@ __global__ void __launch_bounds__(NW * 64)
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
     const int ntiles = tr.nA + tr.nB;
-    TileStager<D, BN, NW> st;
+    const int64_t rs = (int64_t)pr.Hkv * D;
+    PairTile<BN, D, C::NT> kst, vst;
     if (ntiles > 0) {
       const KeyTile kt = tile_at(pr, b, tr, 0, BN);
-      st.load(k, v, kt.row0, min(BN, kt.lim), c, pr.Hkv, tid);
-      st.store(lds, lds + C::K_ELEMS, tid);
+      const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
+      kst.load(k + off, rs, min(BN, kt.lim), tid);
+      vst.load(v + off, rs, min(BN, kt.lim), tid);
+      kst.store_rows(lds, tid);
+      vst.store_trans(lds + C::K_ELEMS, tid);
     }
     __syncthreads();
-    // Swizzle of the V^T rows this lane reads, one per 32-dim block.
-    int vsw[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) vsw[db] = vt_swz<BN>(db * 32 + l32);
 
     for (int it = 0; it < ntiles; ++it) {
       const int cur = it & 1;
       if (it + 1 < ntiles) {
         const KeyTile nx = tile_at(pr, b, tr, it + 1, BN);
-        st.load(k, v, nx.row0, min(BN, nx.lim), c, pr.Hkv, tid);
+        const int64_t off = (int64_t)nx.row0 * rs + (int64_t)c * D;
+        kst.load(k + off, rs, min(BN, nx.lim), tid);
+        vst.load(v + off, rs, min(BN, nx.lim), tid);
       }
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
@@ -250,12 +174,14 @@ __global__ void __launch_bounds__(NW * 64)
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int ks = 0; ks < K16; ++ks) {
-            const int d = db * 32 + l32;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + d * BN + (((2 * ks + hf) ^ vsw[db]) << 3));
+            const bf16x8 a = trans_read<BN>(Vt, db * 32 + l32, ks, hf);
             acc[db] = mfma32(a, pB[ks], acc[db]);
           }
       }
-      if (it + 1 < ntiles) st.store(lds + (cur ^ 1) * C::STAGE, lds + (cur ^ 1) * C::STAGE + C::K_ELEMS, tid);
+      if (it + 1 < ntiles) {
+        kst.store_rows(lds + (cur ^ 1) * C::STAGE, tid);
+        vst.store_trans(lds + (cur ^ 1) * C::STAGE + C::K_ELEMS, tid);
+      }
       __syncthreads();
     }
   }
@@ -289,7 +215,7 @@ struct FwdPlan {
 FwdPlan plan(const Problem& pr) {
   FwdPlan p;
   p.NW = pr.D <= 128 ? 8 : 4;
-  p.BN = 64;
+  p.BN = pr.D <= 128 ? 64 : 32;
   p.HG = heads_per_block(pr.g, p.NW);
   p.BM = 32 * p.NW / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
@@ -325,7 +251,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, cons
   switch (pr.D) {
     case 64: return run<64, 64, 8>(pr, p, q, k, v, o, lse, stream);
     case 128: return run<128, 64, 8>(pr, p, q, k, v, o, lse, stream);
-    case 256: return run<256, 64, 4>(pr, p, q, k, v, o, lse, stream);
+    case 256: return run<256, 32, 4>(pr, p, q, k, v, o, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }
