@@ -97,6 +97,7 @@ __global__ void __launch_bounds__(NW * 64)
     dlt = delta[(int64_t)h * pr.T + qrow];
   }
   const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -147,6 +148,8 @@ __global__ void __launch_bounds__(NW * 64)
             dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + ro), doB[kk], dp[kb]);
           }
         bf16x8 dsB[K16];
+        const int d0 = qpos - kt.pos0 - 4 * hf;
+        const int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
@@ -155,11 +158,10 @@ __global__ void __launch_bounds__(NW * 64)
             for (int j = 0; j < 8; ++j) {
               const int i = 8 * hs + j;
               float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
-              if (kind == 2) {
-                const int key = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                const int kp = kt.pos0 + key;
-                const bool vis = qvalid && key < kt.lim && kp <= qpos && (pr.W <= 0 || qpos - kp < pr.W);
-                if (!vis) p = 0.f;
+              if (kind == 2) {   // branch-free mask (see the forward)
+                const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+                const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+                p = vis ? p : 0.f;
               }
               dsB[2 * kb + hs][j] = (__bf16)(p * (dp[kb][i] - dlt));
             }
@@ -373,6 +375,7 @@ __global__ void __launch_bounds__(NWK * 64)
 
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
   PairTile<kStageRows, D, C::NT> qst, dost;
   float st_l = INFINITY, st_d = 0.f;     // per-thread stage statistics (threads < 32)
 
@@ -442,6 +445,10 @@ __global__ void __launch_bounds__(NWK * 64)
           dp = mfma32(*reinterpret_cast<const bf16x8*>(DOs + ro), vB[kk], dp);
         }
         bf16x8 pB[2], dsB[2];
+        // query qc (+4*hf) of the stage is visible to this lane's key iff
+        // 0 <= qpos - kpos < window and qc < nrows (branch-free).
+        const int e0 = sq_lo + 4 * hf - kpos;
+        const int n0 = (kvalid ? nrows : 0) - 4 * hf;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * g4 + 4 * hf);
@@ -451,12 +458,11 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;                       // register index
-            const int qi = 8 * g4 + 4 * hf + e;             // query row in the stage
+            const int qc = 8 * g4 + e;                      // query row - 4*hf
             float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
             if (kind == 2) {
-              const int qp = sq_lo + qi;
-              const bool vis = kvalid && qi < nrows && kpos <= qp && (pr.W <= 0 || qp - kpos < pr.W);
-              if (!vis) p = 0.f;
+              const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
+              p = vis ? p : 0.f;
             }
             const float ds = p * (dp[i] - dv4[e]);
             pB[i >> 3][i & 7] = (__bf16)p;

@@ -92,6 +92,7 @@ __global__ void __launch_bounds__(NW * 64)
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;   // visible distance bound
 
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
@@ -134,14 +135,17 @@ __global__ void __launch_bounds__(NW * 64)
             s[kb] = mfma32(a, qB[kk], s[kb]);
           }
         if (kind == 2) {
+          // Branch-free mask: key kc (+4*hf) is visible iff
+          // 0 <= qpos - pos < window (one unsigned compare) and kc < lim.
+          const int d0 = qpos - kt.pos0 - 4 * hf;
+          const int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-              const int kp = kt.pos0 + key;
-              const bool vis = qvalid && key < kt.lim && kp <= qpos && (pr.W <= 0 || qpos - kp < pr.W);
-              if (!vis) s[kb][i] = -INFINITY;
+              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+              s[kb][i] = vis ? s[kb][i] : -INFINITY;
             }
         }
         float mx = -INFINITY;

@@ -32,11 +32,12 @@ def run_case(w, impl=dk.IMPL_AUTO, backward=True):
     torch.cuda.synchronize()
     ref = replicated.replicated_fold(x.q, x.k, x.v, x.do, w.n_resp, w.prompt_len, w.resp_len,
                                      w.window, None, x.valid_len, backward=backward)
-    out = {"o": check("o", host(o), ref["o"], w.dtype),
-           "lse": check("lse", host(lse), ref["lse"], w.dtype)}
+    uv = w.value_scale == 1.0
+    out = {"o": check("o", host(o), ref["o"], w.dtype, uv),
+           "lse": check("lse", host(lse), ref["lse"], w.dtype, uv)}
     if backward:
         for name, g in zip(("dq", "dk", "dv"), grads):
-            out[name] = check(name, host(g), ref[name], w.dtype)
+            out[name] = check(name, host(g), ref[name], w.dtype, uv)
     print({k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in out.items()}, flush=True)
     return o, lse, grads
 
