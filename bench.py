@@ -1,0 +1,244 @@
+"""Benchmark of the shared-prompt (DualKV) attention hot path on one MI355X.
+
+One step = the per-micro-batch path of one attention layer:
+  1. repack GATHER of the micro-batch's per-token rows (token id, position,
+     loss mask, advantage: 16 bytes per token) from N(P+R) to P+NR rows;
+  2. forward  (dualkv_fwd)  -> O, LSE;
+  3. backward (dualkv_bwd)  -> dQ, dK, dV (delta, dq, dkdv, slot reduction);
+  4. repack SCATTER of per-token fp32 outputs back to N(P+R) rows.
+Inputs are resident in HBM before the timed region.  `value` is useful
+fwd+bwd TFLOP/s: visible (query, key) pairs of the packed layout times
+14*D*Hq, divided by the measured step time.
+
+Also reported: forward / backward alone, the same library on the replicated
+N(P+R) layout (P'=0, R'=P+R, valid lengths P+L_n: N independent causal
+sequences) and the speedup over it, the dominant kernel's roofline (HIP
+events bracketing its launches inside the timed steps), and the fp64 CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--no-replicated", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def timed(fn, steps, torch):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def cpu_baseline(w, x, seconds):
+    """The fp64 oracle on a bounded sample: replicated sequences n = 0, 1, ...
+    of KV head 0 (all its query heads), forward + backward, until `seconds`
+    have passed.  Rate in useful TFLOP/s of the pairs computed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import replicated
+    from shared_prompt_exact_amd import workcount
+
+    g = w.n_q_heads // w.n_kv_heads
+    L = [w.resp_len] * w.n_resp if x.valid_len is None else [int(a) for a in x.valid_len]
+    done, t0, flops = 0, time.perf_counter(), 0
+    while done < w.n_resp:
+        n = done
+        idx = replicated.sequence_rows(n, w.n_resp, w.prompt_len, w.resp_len)
+        seq_valid = w.prompt_len + L[n]
+        replicated.causal_sequence(x.q[idx].astype(np.float64), x.k[idx].astype(np.float64),
+                                   x.v[idx].astype(np.float64), x.do[idx].astype(np.float64),
+                                   seq_valid, w.window, None, 1024, kv_heads=[0])
+        pairs = workcount.replicated_pairs(1, w.prompt_len, L[n], w.window)
+        flops += 14 * pairs * g * w.head_dim
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 oracle (replicated causal attention + analytic backward), KV head 0 "
+                       f"of {w.n_kv_heads} with its {g} query heads, {done} of {w.n_resp} sequences "
+                       f"of {w.prompt_len}+R tokens, {dt:.1f} s; rate counts useful pairs of the sample")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention "
+              "layer is sharded across GPUs by data parallelism over prompt groups, "
+              "see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import shared_prompt_exact_amd as dk
+    import workloads
+    from shared_prompt_exact_amd import workcount
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    N, P, R, D, Hq, Hkv, Wn = (w.n_resp, w.prompt_len, w.resp_len, w.head_dim, w.n_q_heads,
+                               w.n_kv_heads, w.window)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = workloads.generate(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to = lambda a: torch.from_numpy(a).to(tdt).to(dev)
+    q, k, v, do = to(x.q), to(x.k), to(x.v), to(x.do)
+    valid = None if x.valid_len is None else torch.from_numpy(x.valid_len).to(dev)
+    L = [R] * N if x.valid_len is None else x.valid_len.tolist()
+
+    pairs = workcount.visible_pairs(N, P, R, Wn, L)
+    rep_pairs = workcount.replicated_pairs(N, P, R, Wn, L)
+    fl = workcount.flops(pairs, Hq, D)
+
+    # per-micro-batch token rows (id, position, loss mask, advantage bits)
+    g = torch.Generator().manual_seed(w.seed)
+    tok_rep = torch.randint(0, 2 ** 31 - 1, (N * (P + R), 4), generator=g, dtype=torch.int32).to(dev)
+    tok_packed = torch.empty((P + N * R, 4), dtype=torch.int32, device=dev)
+    tok_out_packed = torch.zeros((P + N * R,), dtype=torch.float32, device=dev)
+    tok_out_rep = torch.empty((N * (P + R),), dtype=torch.float32, device=dev)
+
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, q.shape[0]), dtype=torch.float32, device=dev)
+    dq, dkk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    kw = dict(window=Wn, valid_len=valid)
+    ws = torch.empty(max(256, dk.dualkv_bwd_workspace_bytes(q, k, N, P, R, **kw)), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        dk.dualkv_fwd(q, k, v, N, P, R, out=o, lse=lse, **kw)
+
+    def bwd():
+        dk.dualkv_bwd(q, k, v, o, lse, do, N, P, R, workspace=ws, dq=dq, dk=dkk, dv=dv, **kw)
+
+    def step():
+        dk.dualkv_repack(tok_rep, N, P, R, dk.DUALKV_GATHER, out=tok_packed)
+        fwd()
+        bwd()
+        dk.dualkv_repack(tok_out_packed, N, P, R, dk.DUALKV_SCATTER, out=tok_out_rep)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps, torch)
+    ms_fwd = timed(fwd, args.steps, torch)
+    ms_bwd = timed(bwd, args.steps, torch)
+    print(f"[bench] step {ms_step:.3f} ms  fwd {ms_fwd:.3f}  bwd {ms_bwd:.3f}", file=sys.stderr, flush=True)
+
+    # Kernel durations from HIP events bracketing each launch (timed steps).
+    dk.dualkv_profile_start()
+    for _ in range(args.steps):
+        step()
+    prof = dk.dualkv_profile_stop()
+    kernel_flops = {"fwd": fl["kernel_fwd"], "bwd_dq": fl["kernel_bwd_dq"], "bwd_dkdv": fl["kernel_bwd_dkdv"]}
+    kernels = {name: {"launches": n, "avg_ms": ms / n} for name, (n, ms) in prof.items()}
+    for name, kf in kernel_flops.items():
+        if name in kernels:
+            kernels[name]["tflops"] = kf / (kernels[name]["avg_ms"] * 1e-3) / 1e12
+    dom = max(kernel_flops, key=lambda n: kernels.get(n, {"avg_ms": 0})["avg_ms"] * kernels.get(n, {"launches": 0})["launches"])
+    dom_ach = kernels[dom]["tflops"]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    # Repack of hidden-state-sized rows (Hq*D bf16 per token), HBM bound.
+    rep_rows = dk.dualkv_repack(do, N, P, R, dk.DUALKV_SCATTER)
+    packed_rows = torch.empty_like(do)
+    ms_gather = timed(lambda: dk.dualkv_repack(rep_rows, N, P, R, dk.DUALKV_GATHER, out=packed_rows), args.steps, torch)
+    ms_scatter = timed(lambda: dk.dualkv_repack(do, N, P, R, dk.DUALKV_SCATTER, out=rep_rows), args.steps, torch)
+    row_b = Hq * D * do.element_size()
+    gather_gbs = 2 * (P + N * R) * row_b / (ms_gather * 1e-3) / 1e9
+    scatter_gbs = ((P + N * R) + N * (P + R)) * row_b / (ms_scatter * 1e-3) / 1e9
+    del rep_rows, packed_rows
+
+    # Same kernels on the replicated layout: N independent causal sequences.
+    rep = None
+    if not args.no_replicated:
+        print("[bench] replicated layout", file=sys.stderr, flush=True)
+        qr, kr, vr, dor = (dk.dualkv_repack(t, N, P, R, dk.DUALKV_SCATTER) for t in (q, k, v, do))
+        vr_len = torch.tensor([P + l for l in L], dtype=torch.int32, device=dev)
+        rkw = dict(window=Wn, valid_len=vr_len)
+        orr = torch.empty_like(qr)
+        lr = torch.empty((Hq, qr.shape[0]), dtype=torch.float32, device=dev)
+        dqr, dkr, dvr = torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(vr)
+        wsr = torch.empty(max(256, dk.dualkv_bwd_workspace_bytes(qr, kr, N, 0, P + R, **rkw)),
+                          dtype=torch.uint8, device=dev)
+
+        def rstep():
+            dk.dualkv_fwd(qr, kr, vr, N, 0, P + R, out=orr, lse=lr, **rkw)
+            dk.dualkv_bwd(qr, kr, vr, orr, lr, dor, N, 0, P + R, workspace=wsr, dq=dqr, dk=dkr, dv=dvr, **rkw)
+
+        rsteps = max(2, args.steps // 2)
+        rstep()
+        ms_rep = timed(rstep, rsteps, torch)
+        ms_rep_fwd = timed(lambda: dk.dualkv_fwd(qr, kr, vr, N, 0, P + R, out=orr, lse=lr, **rkw), rsteps, torch)
+        rep = {"ms_fwd_bwd": round(ms_rep, 3), "ms_fwd": round(ms_rep_fwd, 3),
+               "tflops_fwd_bwd": round(14 * rep_pairs * Hq * D / (ms_rep * 1e-3) / 1e12, 2),
+               "speedup_fwd_bwd": round(ms_rep / (ms_fwd + ms_bwd), 3),
+               "speedup_fwd": round(ms_rep_fwd / ms_fwd, 3),
+               "speedup_step": round(ms_rep / ms_step, 3)}
+        del qr, kr, vr, dor, orr, lr, dqr, dkr, dvr, wsr
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+
+    value = fl["fwd_bwd"] / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "DualKV attn fwd+bwd TFLOP/s, % bf16 MFMA peak, speedup vs replicated layout",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded i.i.d. Gaussian activations of the layer shape)",
+        "config": {"workload": w.name, "N": N, "P": P, "R": R, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "window": Wn, "packed_tokens": P + N * R,
+                   "replicated_tokens": N * (P + R)},
+        "pct_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "fwd": {"ms": round(ms_fwd, 3), "tflops": round(fl["fwd"] / (ms_fwd * 1e-3) / 1e12, 2)},
+        "bwd": {"ms": round(ms_bwd, 3), "tflops": round(fl["bwd"] / (ms_bwd * 1e-3) / 1e12, 2)},
+        "rho": round(workcount.token_ratio(N, P, R), 4),
+        "rho_attn": round(rep_pairs / pairs, 4),
+        "replicated": rep,
+        "kernels": {k_: {kk: round(vv, 4) for kk, vv in d.items()} for k_, d in kernels.items()},
+        "repack_hidden_rows": {"gather_GBs": round(gather_gbs, 1), "scatter_GBs": round(scatter_gbs, 1),
+                               "row_bytes": row_b},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

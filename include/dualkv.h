@@ -29,7 +29,8 @@
  *
  * Ownership: every pointer is caller-owned device memory (except `p`, a
  * host pointer).  The library never allocates or frees memory, keeps no
- * pointer after a call returns, and holds no mutable global state.
+ * pointer after a call returns, and holds no mutable global state apart
+ * from the opt-in launch profiler declared at the end of this header.
  * Streams: `stream` is a hipStream_t (NULL = default stream); all work is
  * enqueued on it and the call returns after enqueueing.
  * Errors: arguments are validated on the host before anything is
@@ -71,7 +72,7 @@ typedef struct dualkv_params {
   int32_t n_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;      /* D: 1..512 (scalar); 64, 128, 256, 512 (MFMA) */
   int32_t window;        /* <= 0: none; else keys with pos_q - pos_k < window */
-  float softmax_scale;   /* 0: 1/sqrt(D) */
+  float softmax_scale;   /* > 0, or 0 for 1/sqrt(D); negative is invalid */
   int32_t dtype;         /* DUALKV_F32 or DUALKV_BF16, shared by every tensor
                             argument except LSE (always fp32) */
   int32_t impl;          /* DUALKV_IMPL_* */
@@ -128,6 +129,24 @@ int dualkv_bwd(const dualkv_params* p, const void* q, const void* k,
 
 /* Static, human-readable text for a status code. */
 const char* dualkv_strerror(int status);
+
+/*
+ * Launch profiler for measurement tools (results are unaffected).
+ * dualkv_profile_start() clears earlier records and starts bracketing
+ * every kernel the library launches with two HIP events on the launch
+ * stream.  dualkv_profile_stop() stops recording, waits for the recorded
+ * events and aggregates elapsed time per kernel name; it returns
+ * DUALKV_ERR_HIP if an event could not be read.  dualkv_profile_count()
+ * then gives the number of kernel names and dualkv_profile_kernel(i, ...)
+ * the name (static storage, valid until the next start), launch count and
+ * total milliseconds of entry i (DUALKV_ERR_INVALID_ARGUMENT for a bad i or
+ * null output).  The profiler is process-wide state guarded by a mutex;
+ * it is the only mutable state of the library and is off by default.
+ */
+int dualkv_profile_start(void);
+int dualkv_profile_stop(void);
+int dualkv_profile_count(void);
+int dualkv_profile_kernel(int index, const char** name, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

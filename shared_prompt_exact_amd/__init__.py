@@ -64,6 +64,11 @@ def load_library():
     lib.dualkv_bwd.restype = ctypes.c_int
     lib.dualkv_strerror.argtypes = [ctypes.c_int]
     lib.dualkv_strerror.restype = ctypes.c_char_p
+    lib.dualkv_profile_start.argtypes = []
+    lib.dualkv_profile_stop.argtypes = []
+    lib.dualkv_profile_count.argtypes = []
+    lib.dualkv_profile_kernel.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
     _lib = lib
     return lib
 
@@ -180,3 +185,21 @@ def dualkv_bwd(q, k, v, o, lse, dout, n_resp, prompt_len, resp_len, window=0, so
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()),
            "dualkv_bwd")
     return dq, dk, dv
+
+
+def dualkv_profile_start():
+    """Start bracketing every library launch with HIP events."""
+    _check(load_library().dualkv_profile_start(), "dualkv_profile_start")
+
+
+def dualkv_profile_stop():
+    """Stop, wait for the events and return {kernel: (launches, total_ms)}."""
+    lib = load_library()
+    _check(lib.dualkv_profile_stop(), "dualkv_profile_stop")
+    out = {}
+    for i in range(lib.dualkv_profile_count()):
+        name, n, ms = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        _check(lib.dualkv_profile_kernel(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+               "dualkv_profile_kernel")
+        out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out

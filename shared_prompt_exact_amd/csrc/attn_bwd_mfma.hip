@@ -605,13 +605,13 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   const uint16_t* do16 = static_cast<const uint16_t*>(dout);
   hipError_t e;
   if (p.nwg_dq > 0) {
-    e = launch(bwd_dq_kernel<D, kDqBN, NW>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
+    e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
                stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
                static_cast<uint16_t*>(dq));
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    e = launch(bwd_dkdv_kernel<D, NWK>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
+    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
                stream, pr, p.sh, q16, k16, v16, do16, lse, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
@@ -620,7 +620,7 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
     const int64_t n4 = (int64_t)pr.P * pr.Hkv * D / 4;
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    e = launch(reduce_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pk, pv,
+    e = launch("bwd_reduce", reduce_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pk, pv,
                p.sh.slots, n4, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     if (e != hipSuccess) return e;
   }

@@ -234,7 +234,7 @@ hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k
   using C = FwdCfg<D, BN, NW>;
   static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  return launch(fwd_mfma_kernel<D, BN, NW>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
+  return launch("fwd", fwd_mfma_kernel<D, BN, NW>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
                 stream, pr, p.HG, p.nbP, p.nbR, static_cast<const uint16_t*>(q),
                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                 static_cast<uint16_t*>(o), lse);

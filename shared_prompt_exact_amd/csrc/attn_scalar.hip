@@ -307,9 +307,9 @@ hipError_t launch_fwd_scalar(const Problem& pr, int dtype, const void* q, const 
                              const void* v, void* o, float* lse, hipStream_t stream) {
   const dim3 grid(blocks_for((int64_t)pr.T * pr.Hq)), block(64 * kWaves);
   if (dtype == DUALKV_F32)
-    return launch(fwd_scalar_kernel<float>, grid, block, 0, stream, pr, (const float*)q,
+    return launch("fwd_scalar", fwd_scalar_kernel<float>, grid, block, 0, stream, pr, (const float*)q,
                   (const float*)k, (const float*)v, (float*)o, lse);
-  return launch(fwd_scalar_kernel<uint16_t>, grid, block, 0, stream, pr, (const uint16_t*)q,
+  return launch("fwd_scalar", fwd_scalar_kernel<uint16_t>, grid, block, 0, stream, pr, (const uint16_t*)q,
                 (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse);
 }
 
@@ -317,9 +317,9 @@ hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const v
                             const float* lse, float* delta, hipStream_t stream) {
   const dim3 grid(blocks_for((int64_t)pr.T * pr.Hq)), block(64 * kWaves);
   if (dtype == DUALKV_F32)
-    return launch(delta_kernel<float>, grid, block, 0, stream, pr, (const float*)o,
+    return launch("bwd_delta", delta_kernel<float>, grid, block, 0, stream, pr, (const float*)o,
                   (const float*)dout, lse, delta);
-  return launch(delta_kernel<uint16_t>, grid, block, 0, stream, pr, (const uint16_t*)o,
+  return launch("bwd_delta", delta_kernel<uint16_t>, grid, block, 0, stream, pr, (const uint16_t*)o,
                 (const uint16_t*)dout, lse, delta);
 }
 
@@ -331,18 +331,18 @@ hipError_t launch_bwd_scalar(const Problem& pr, int dtype, const void* q, const 
   const dim3 gq(blocks_for((int64_t)pr.T * pr.Hq)), gk(blocks_for((int64_t)pr.T * pr.Hkv));
   const dim3 block(64 * kWaves);
   if (dtype == DUALKV_F32) {
-    e = launch(dq_scalar_kernel<float>, gq, block, 0, stream, pr, (const float*)q, (const float*)k,
+    e = launch("bwd_dq_scalar", dq_scalar_kernel<float>, gq, block, 0, stream, pr, (const float*)q, (const float*)k,
                (const float*)v, (const float*)dout, lse, (const float*)delta, (float*)dq);
     if (e != hipSuccess) return e;
-    return launch(dkdv_scalar_kernel<float>, gk, block, 0, stream, pr, (const float*)q,
+    return launch("bwd_dkdv_scalar", dkdv_scalar_kernel<float>, gk, block, 0, stream, pr, (const float*)q,
                   (const float*)k, (const float*)v, (const float*)dout, lse, (const float*)delta,
                   (float*)dk, (float*)dv);
   }
-  e = launch(dq_scalar_kernel<uint16_t>, gq, block, 0, stream, pr, (const uint16_t*)q,
+  e = launch("bwd_dq_scalar", dq_scalar_kernel<uint16_t>, gq, block, 0, stream, pr, (const uint16_t*)q,
              (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
              (const float*)delta, (uint16_t*)dq);
   if (e != hipSuccess) return e;
-  return launch(dkdv_scalar_kernel<uint16_t>, gk, block, 0, stream, pr, (const uint16_t*)q,
+  return launch("bwd_dkdv_scalar", dkdv_scalar_kernel<uint16_t>, gk, block, 0, stream, pr, (const uint16_t*)q,
                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
                 (const float*)delta, (uint16_t*)dk, (uint16_t*)dv);
 }

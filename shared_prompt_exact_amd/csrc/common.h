@@ -49,17 +49,26 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Opt-in launch profiler (profile.hip): brackets launches with HIP events.
+bool profiling_on();
+int profile_begin(const char* name, hipStream_t stream);
+void profile_end(int slot, hipStream_t stream);
+
 // Launch a kernel and return the runtime's status for that launch (the
 // status of hipLaunchKernel itself, not a stale error of an earlier call).
+// `name` labels the launch for the profiler.
 template <typename... KArgs, typename... Args>
-static inline hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
-                                hipStream_t stream, Args... args) {
+static inline hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 grid, dim3 block,
+                                size_t shmem, hipStream_t stream, Args... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
   auto go = [&](KArgs... conv) -> hipError_t {
     void* ptrs[] = {static_cast<void*>(&conv)...};
     return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, stream);
   };
-  return go(static_cast<KArgs>(args)...);
+  const int slot = profiling_on() ? profile_begin(name, stream) : -1;
+  const hipError_t e = go(static_cast<KArgs>(args)...);
+  if (slot >= 0) profile_end(slot, stream);
+  return e;
 }
 
 // ---- launchers implemented in the kernel translation units -------------

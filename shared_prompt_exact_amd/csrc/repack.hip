@@ -53,7 +53,7 @@ hipError_t go(const void* src, void* dst, int64_t row_bytes, int64_t n_rows, int
   int64_t rows_per_iter = row_elems >= 256 ? 1 : 256 / row_elems;
   int64_t blocks = (n_rows + rows_per_iter - 1) / rows_per_iter;
   if (blocks > 256 * 64) blocks = 256 * 64;
-  return launch(repack_kernel<V>, dim3((unsigned)blocks), dim3(256), 0, stream,
+  return launch("repack", repack_kernel<V>, dim3((unsigned)blocks), dim3(256), 0, stream,
                 static_cast<const V*>(src), static_cast<V*>(dst), row_elems, n_rows, N, P, R,
                 direction);
 }
