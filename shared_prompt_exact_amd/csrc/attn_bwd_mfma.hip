@@ -203,6 +203,8 @@ template <int D, int NWK>
 struct KvCfg {
   static constexpr int NT = NWK * 64;
   static constexpr int BK = 32 * NWK;            // keys per workgroup
+  static constexpr int VSTR = D + 8;
+  static constexpr int V_ELEMS = BK * VSTR;          // V tile rows (B operand of dP)
   static constexpr int QSTR = D + 8;
   static constexpr int Q_ELEMS = kStageRows * QSTR;   // Q rows
   static constexpr int DO_ELEMS = kStageRows * QSTR;  // dO rows
@@ -210,7 +212,7 @@ struct KvCfg {
   static constexpr int DOT_ELEMS = D * kStageRows;    // dO^T
   static constexpr int STAT = 2 * kStageRows * 2;     // lse2, delta (fp32 as 2 x u16)
   static constexpr int STAGE = Q_ELEMS + DO_ELEMS + QT_ELEMS + DOT_ELEMS + STAT;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int LDS_BYTES = (V_ELEMS + 2 * STAGE) * 2;
 };
 
 // Work item of the dK/dV kernel.
@@ -327,25 +329,30 @@ __global__ void __launch_bounds__(NWK * 64)
   const int kp_lo = posoff + it.k0;
   const int kp_hi = posoff + it.k0 + min(C::BK, max(klim, 1)) - 1;
 
-  // ---- this wave's 32 keys as B operands (K^T and V^T slices)
+  // ---- this wave's 32 keys: K^T as B operands in registers; the whole
+  // V tile row-major in LDS (B operand of dP, read per use) so that a wave
+  // fits in 256 registers and two waves share each SIMD.
   const int wk0 = 32 * wave;                          // first key of the wave in the tile
   const int my_k = wk0 + l32;
   const bool kvalid = my_k < klim;
   const int kpos = kp_lo + my_k;
   const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
   const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KT], vB[KT];
+  bf16x8 kB[KT];
 #pragma unroll
   for (int kk = 0; kk < KT; ++kk) {
-    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    if (kvalid) {
-      const int64_t off = krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf;
-      z = *reinterpret_cast<const uint4*>(k + off);
-      y = *reinterpret_cast<const uint4*>(v + off);
-    }
+    uint4 z = {0, 0, 0, 0};
+    if (kvalid) z = *reinterpret_cast<const uint4*>(k + krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf);
     kB[kk] = __builtin_bit_cast(bf16x8, z);
-    vB[kk] = __builtin_bit_cast(bf16x8, y);
   }
+  uint16_t* Vs = lds;
+  {
+    PairTile<C::BK, D, C::NT> vt;
+    vt.load(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
+            klim > 0 ? min(C::BK, klim) : 0, tid);
+    vt.store_rows(Vs, tid);
+  }
+  uint16_t* const stage_base = lds + C::V_ELEMS;
   const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
@@ -412,14 +419,14 @@ __global__ void __launch_bounds__(NWK * 64)
   int buf = 0;
   if (cur.ok) {
     stage_load(cur);
-    stage_store(lds);
+    stage_store(stage_base);
   }
   __syncthreads();
   while (cur.ok) {
     if (nxt.ok) stage_load(nxt);
     // ---- compute on stage `cur`
     {
-      const uint16_t* Qs = lds + buf * C::STAGE;
+      const uint16_t* Qs = stage_base + buf * C::STAGE;
       const uint16_t* DOs = Qs + C::Q_ELEMS;
       const uint16_t* QT = DOs + C::DO_ELEMS;
       const uint16_t* DOT = QT + C::QT_ELEMS;
@@ -441,8 +448,9 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk) {
           const int ro = l32 * C::QSTR + 16 * kk + 8 * hf;
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Vs + (wk0 + l32) * C::VSTR + 16 * kk + 8 * hf);
           s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ro), kB[kk], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(DOs + ro), vB[kk], dp);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(DOs + ro), vb, dp);
         }
         bf16x8 pB[2], dsB[2];
         // query qc (+4*hf) of the stage is visible to this lane's key iff
@@ -478,7 +486,7 @@ __global__ void __launch_bounds__(NWK * 64)
           }
       }
     }
-    if (nxt.ok) stage_store(lds + (buf ^ 1) * C::STAGE);
+    if (nxt.ok) stage_store(stage_base + (buf ^ 1) * C::STAGE);
     __syncthreads();
     cur = nxt;
     if (nxt.ok) iter_next(pr, nxt, kp_lo, kp_hi);
@@ -540,8 +548,7 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------------ planning
 
-constexpr int kDqBN = 64;
-constexpr int kNWK = 4;
+constexpr int kNWK = 8;   // dK/dV waves per workgroup (2 per SIMD)
 
 struct BwdPlan {
   int NW, HG, BM, nbP, nbR;
@@ -555,7 +562,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 BwdPlan plan(const Problem& pr) {
   BwdPlan p;
-  p.NW = pr.D <= 64 ? 8 : 4;
+  p.NW = 8;
   p.HG = heads_per_block(pr.g, p.NW);
   p.BM = 32 * p.NW / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
@@ -586,7 +593,7 @@ BwdPlan plan(const Problem& pr) {
   return p;
 }
 
-template <int D, int NW, int NWK>
+template <int D, int NW, int NWK, int kDqBN>
 hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, char* ws,
                hipStream_t stream) {
@@ -646,8 +653,8 @@ hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, cons
                                   reinterpret_cast<float*>(ws + p.off_delta), stream);
   if (e != hipSuccess) return e;
   switch (pr.D) {
-    case 64: return run<64, 8, kNWK>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 4, kNWK>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 64: return run<64, 8, kNWK, 64>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, kNWK, 32>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
