@@ -26,7 +26,7 @@
 // The prompt K/V tile is thereby reused by the query blocks of all N
 // responses inside one workgroup, and the N-fold sum never leaves a fixed
 // order, so results are bitwise reproducible.
-#include "tiles.h"
+#include "lds_tiles.h"
 
 namespace dualkv {
 namespace {
@@ -35,24 +35,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------- dq kernel
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NS>
 struct DqCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int KSTR = D + 8;
-  static constexpr int K_ELEMS = BN * KSTR;      // K row-major
-  static constexpr int V_ELEMS = BN * KSTR;      // V row-major
-  static constexpr int KT_ELEMS = D * BN;        // K transposed
-  static constexpr int STAGE = K_ELEMS + V_ELEMS + KT_ELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
+  static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int LDS_BYTES = NS * STAGE * 2;
+  static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
+  static constexpr int BPW = KBLK / NW;
+  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NS>
 __global__ void __launch_bounds__(NW * 64)
     bwd_dq_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   const uint16_t* __restrict__ dout, const float* __restrict__ lse,
                   const float* __restrict__ delta, uint16_t* __restrict__ dq) {
-  using C = DqCfg<D, BN, NW>;
+  using C = DqCfg<D, BN, NW, NS>;
   constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -96,6 +96,8 @@ __global__ void __launch_bounds__(NW * 64)
     lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
     dlt = delta[(int64_t)h * pr.T + qrow];
   }
+  wait_vmcnt<0>();                    // the loop's waits count only tile loads
+  asm volatile("" ::: "memory");
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
 
@@ -109,31 +111,27 @@ __global__ void __launch_bounds__(NW * 64)
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
     const int ntiles = tr.nA + tr.nB;
     const int64_t rs = (int64_t)pr.Hkv * D;
-    PairTile<BN, D, C::NT> kst, vst;
-    if (ntiles > 0) {
-      const KeyTile kt = tile_at(pr, b, tr, 0, BN);
+    auto issue = [&](int t) {
+      const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
-      kst.load(k + off, rs, min(BN, kt.lim), tid);
-      vst.load(v + off, rs, min(BN, kt.lim), tid);
-      kst.store_rows(lds, tid);
-      vst.store_rows(lds + C::K_ELEMS, tid);
-      kst.store_trans(lds + C::K_ELEMS + C::V_ELEMS, tid);
-    }
-    __syncthreads();
+      uint16_t* slot = lds + (t % NS) * C::STAGE;
+      const int nv = min(BN, kt.lim);
+      dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
+      dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < ntiles) issue(t);
     for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < ntiles) {
-        const KeyTile nx = tile_at(pr, b, tr, it + 1, BN);
-        const int64_t off = (int64_t)nx.row0 * rs + (int64_t)c * D;
-        kst.load(k + off, rs, min(BN, nx.lim), tid);
-        vst.load(v + off, rs, min(BN, nx.lim), tid);
-      }
+      if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
+      else wait_vmcnt<0>();
+      block_sync();
+      if (it + NS - 1 < ntiles) issue(it + NS - 1);
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
       if (kind != 0) {
-        const uint16_t* Ks = lds + cur * C::STAGE;
+        const uint16_t* Ks = lds + (it % NS) * C::STAGE;
         const uint16_t* Vs = Ks + C::K_ELEMS;
-        const uint16_t* Kt = Vs + C::V_ELEMS;
         f32x16 s[NB32], dp[NB32];
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
@@ -143,9 +141,8 @@ __global__ void __launch_bounds__(NW * 64)
         for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb) {
-            const int ro = (kb * 32 + l32) * C::KSTR + 16 * kk + 8 * hf;
-            s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + ro), qB[kk], s[kb]);
-            dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(Vs + ro), doB[kk], dp[kb]);
+            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, kk, hf), qB[kk], s[kb]);
+            dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, kk, hf), doB[kk], dp[kb]);
           }
         bf16x8 dsB[K16];
         const int d0 = qpos - kt.pos0 - 4 * hf;
@@ -169,15 +166,8 @@ __global__ void __launch_bounds__(NW * 64)
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int ks = 0; ks < K16; ++ks)
-            acc[db] = mfma32(trans_read<BN>(Kt, db * 32 + l32, ks, hf), dsB[ks], acc[db]);
+            acc[db] = mfma32(trans_operand<D>(Ks, 0, db * 32, ks, lane), dsB[ks], acc[db]);
       }
-      if (it + 1 < ntiles) {
-        uint16_t* nb = lds + (cur ^ 1) * C::STAGE;
-        kst.store_rows(nb, tid);
-        vst.store_rows(nb + C::K_ELEMS, tid);
-        kst.store_trans(nb + C::K_ELEMS + C::V_ELEMS, tid);
-      }
-      __syncthreads();
     }
   }
 
@@ -199,20 +189,19 @@ __global__ void __launch_bounds__(NW * 64)
 
 constexpr int kStageRows = 32;
 
-template <int D, int NWK>
+template <int D, int NWK, int NS>
 struct KvCfg {
-  static constexpr int NT = NWK * 64;
-  static constexpr int BK = 32 * NWK;            // keys per workgroup
-  static constexpr int VSTR = D + 8;
-  static constexpr int V_ELEMS = BK * VSTR;          // V tile rows (B operand of dP)
-  static constexpr int QSTR = D + 8;
-  static constexpr int Q_ELEMS = kStageRows * QSTR;   // Q rows
-  static constexpr int DO_ELEMS = kStageRows * QSTR;  // dO rows
-  static constexpr int QT_ELEMS = D * kStageRows;     // Q^T
-  static constexpr int DOT_ELEMS = D * kStageRows;    // dO^T
-  static constexpr int STAT = 2 * kStageRows * 2;     // lse2, delta (fp32 as 2 x u16)
-  static constexpr int STAGE = Q_ELEMS + DO_ELEMS + QT_ELEMS + DOT_ELEMS + STAT;
-  static constexpr int LDS_BYTES = (V_ELEMS + 2 * STAGE) * 2;
+  static constexpr int BK = 32 * NWK;               // keys per workgroup
+  static constexpr int V_ELEMS = BK * D;            // V tile (B operand of dP), loaded once
+  static constexpr int Q_ELEMS = kStageRows * D;    // Q stage rows
+  static constexpr int DO_ELEMS = kStageRows * D;   // dO stage rows
+  static constexpr int STAT = 2 * kStageRows * 2;   // LSE and delta, fp32 (in u16 units)
+  static constexpr int STAGE = Q_ELEMS + DO_ELEMS + STAT;
+  static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2;
+  static constexpr int VBPW = V_ELEMS * 2 / 1024 / NWK;     // V blocks per wave
+  static constexpr int QBLK = Q_ELEMS * 2 / 1024;           // blocks per Q (or dO) stage tile
+  static constexpr int SBPW = 2 * QBLK / NWK;               // stage blocks per wave
+  static_assert(V_ELEMS * 2 % (1024 * NWK) == 0 && 2 * QBLK % NWK == 0, "even split");
 };
 
 // Work item of the dK/dV kernel.
@@ -223,16 +212,12 @@ struct KvItem {
   int slot;       // prompt tiles: slot (0 = prompt queries, s >= 1 = responses)
 };
 
-// Query segments visited by an item and their row ranges.
-struct QueryPlan {
-  int first, last;   // segment ids (-1 = prompt) in ascending order
-};
-
 // Walks (segment, 32-row stage, query head) in a fixed order.
 struct StageIter {
   int seg, seg_last;
   int r, r_end;       // current stage row and the segment's row bound
   int h, h0, h1;
+  int svalid;         // valid rows of the current segment (read once per segment)
   bool ok;
 };
 
@@ -245,12 +230,13 @@ struct KvShape {
 // Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
 // positions) of the item; lo is rounded down to a stage boundary.
 __device__ __forceinline__ void seg_rows(const Problem& pr, int seg, int kp_lo, int kp_hi, int& lo,
-                                         int& hi) {
+                                         int& hi, int& Lv) {
   if (seg < 0) {
     lo = (kp_lo / kStageRows) * kStageRows;
     hi = pr.W > 0 ? min(pr.P, kp_hi + pr.W) : pr.P;
+    Lv = pr.P;
   } else {
-    const int Lv = resp_valid(pr, seg);
+    Lv = resp_valid(pr, seg);
     const int rlo = max(0, kp_lo - pr.P);
     lo = (rlo / kStageRows) * kStageRows;
     hi = Lv;
@@ -261,11 +247,12 @@ __device__ __forceinline__ void seg_rows(const Problem& pr, int seg, int kp_lo, 
 __device__ __forceinline__ void iter_fix(const Problem& pr, StageIter& s, int kp_lo, int kp_hi) {
   // move to the first non-empty segment at or after s.seg
   while (s.seg <= s.seg_last) {
-    int lo, hi;
-    seg_rows(pr, s.seg, kp_lo, kp_hi, lo, hi);
+    int lo, hi, Lv;
+    seg_rows(pr, s.seg, kp_lo, kp_hi, lo, hi, Lv);
     if (s.r < lo) s.r = lo;
     if (s.r < hi) {
       s.r_end = hi;
+      s.svalid = Lv;
       s.ok = true;
       return;
     }
@@ -285,7 +272,7 @@ __device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int k
   iter_fix(pr, s, kp_lo, kp_hi);
 }
 
-template <int D, int NWK>
+template <int D, int NWK, int NS>
 __global__ void __launch_bounds__(NWK * 64)
     bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -293,7 +280,7 @@ __global__ void __launch_bounds__(NWK * 64)
                     const float* __restrict__ delta, uint16_t* __restrict__ dk,
                     uint16_t* __restrict__ dv, float* __restrict__ part_k,
                     float* __restrict__ part_v) {
-  using C = KvCfg<D, NWK>;
+  using C = KvCfg<D, NWK, NS>;
   constexpr int KT = D / 16, DB = D / 32;
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -329,8 +316,8 @@ __global__ void __launch_bounds__(NWK * 64)
   const int kp_lo = posoff + it.k0;
   const int kp_hi = posoff + it.k0 + min(C::BK, max(klim, 1)) - 1;
 
-  // ---- this wave's 32 keys: K^T as B operands in registers; the whole
-  // V tile row-major in LDS (B operand of dP, read per use) so that a wave
+  // ---- this wave's 32 keys: K^T as B operands in registers; the V tile
+  // row-major in LDS (B operand of dP).  With K only in registers a wave
   // fits in 256 registers and two waves share each SIMD.
   const int wk0 = 32 * wave;                          // first key of the wave in the tile
   const int my_k = wk0 + l32;
@@ -345,14 +332,13 @@ __global__ void __launch_bounds__(NWK * 64)
     if (kvalid) z = *reinterpret_cast<const uint4*>(k + krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf);
     kB[kk] = __builtin_bit_cast(bf16x8, z);
   }
-  uint16_t* Vs = lds;
-  {
-    PairTile<C::BK, D, C::NT> vt;
-    vt.load(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
-            klim > 0 ? min(C::BK, klim) : 0, tid);
-    vt.store_rows(Vs, tid);
-  }
+  wait_vmcnt<0>();                    // the loop's waits count only LDS loads
+  asm volatile("" ::: "memory");
+  const uint16_t* Vs = lds;
   uint16_t* const stage_base = lds + C::V_ELEMS;
+  if (klim > 0)
+    dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
+                min(C::BK, klim), lds, wave * C::VBPW, C::VBPW, lane);
   const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
@@ -362,79 +348,74 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dKt[db][i] = dVt[db][i] = 0.f;
 
-  // ---- the query stages of this item
-  StageIter cur;
+  // ---- the query stages of this item, NS-1 stages ahead in an LDS ring
+  StageIter s0;
   if (it.seg >= 0) {
-    cur.seg = cur.seg_last = it.seg;
+    s0.seg = s0.seg_last = it.seg;
   } else if (it.slot == 0) {
-    cur.seg = cur.seg_last = -1;
+    s0.seg = s0.seg_last = -1;
   } else {
-    cur.seg = (it.slot - 1) * sh.per_slot;
-    cur.seg_last = min(pr.N, it.slot * sh.per_slot) - 1;
+    s0.seg = (it.slot - 1) * sh.per_slot;
+    s0.seg_last = min(pr.N, it.slot * sh.per_slot) - 1;
   }
-  cur.h0 = cur.h = c * pr.g;
-  cur.h1 = (c + 1) * pr.g;
-  cur.r = 0;
-  cur.ok = false;
-  if (klim > 0) iter_fix(pr, cur, kp_lo, kp_hi);
-  StageIter nxt = cur;
-  if (nxt.ok) iter_next(pr, nxt, kp_lo, kp_hi);
+  s0.h0 = s0.h = c * pr.g;
+  s0.h1 = (c + 1) * pr.g;
+  s0.r = 0;
+  s0.ok = false;
+  if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
+  StageIter s1 = s0;
+  if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
+  StageIter s2 = s1;
+  if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+  static_assert(NS == 3, "the ring below keeps two stages in flight");
 
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
-  PairTile<kStageRows, D, C::NT> qst, dost;
-  float st_l = INFINITY, st_d = 0.f;     // per-thread stage statistics (threads < 32)
+  const bool stat_wave = wave == NWK - 1;    // also loads the stage's LSE / delta
 
-  auto stage_load = [&](const StageIter& s) {
-    const int sb = s.seg < 0 ? 0 : pr.P + s.seg * pr.R;
-    const int svalid = s.seg < 0 ? pr.P : resp_valid(pr, s.seg);
-    const int n = min(kStageRows, svalid - s.r);
-    const int64_t off = ((int64_t)sb + s.r) * qstride + (int64_t)s.h * D;
-    qst.load(q + off, qstride, n, tid);
-    dost.load(dout + off, qstride, n, tid);
-    if (tid < kStageRows) {
-      st_l = INFINITY;
-      st_d = 0.f;
-      if (tid < n) {
-        const int64_t idx = (int64_t)s.h * pr.T + sb + s.r + tid;
-        const float Lr = lse[idx];
-        st_l = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
-        st_d = delta[idx];
-      }
+  auto issue = [&](const StageIter& st, int slot) {
+    const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
+    const int n = min(kStageRows, st.svalid - st.r);
+    const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
+    uint16_t* buf = stage_base + slot * C::STAGE;
+    // blocks w, w + NWK, ... of [Q blocks, dO blocks]
+#pragma unroll
+    for (int j = 0; j < C::SBPW; ++j) {
+      const int blk = wave + j * NWK;
+      if (blk < C::QBLK) dma_rows<D>(q + off, qstride, n, buf, blk, 1, lane);
+      else dma_rows<D>(dout + off, qstride, n, buf + C::Q_ELEMS, blk - C::QBLK, 1, lane);
     }
-  };
-  auto stage_store = [&](uint16_t* buf) {
-    qst.store_rows(buf, tid);
-    dost.store_rows(buf + C::Q_ELEMS, tid);
-    qst.store_trans(buf + C::Q_ELEMS + C::DO_ELEMS, tid);
-    dost.store_trans(buf + C::Q_ELEMS + C::DO_ELEMS + C::QT_ELEMS, tid);
-    float* stat = reinterpret_cast<float*>(buf + C::Q_ELEMS + C::DO_ELEMS + C::QT_ELEMS + C::DOT_ELEMS);
-    if (tid < kStageRows) {
-      stat[tid] = st_l;
-      stat[kStageRows + tid] = st_d;
+    if (stat_wave) {
+      // 64 lanes x 4 bytes: LSE of the 32 rows, then their delta
+      const int row = sb + st.r + min(lane & 31, n - 1);
+      const float* src = (lane < 32 ? lse : delta) + (int64_t)st.h * pr.T + row;
+      const unsigned ldsaddr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
+          __attribute__((address_space(3))) void*)(buf + C::Q_ELEMS + C::DO_ELEMS));
+      asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
     }
   };
 
-  int buf = 0;
-  if (cur.ok) {
-    stage_load(cur);
-    stage_store(stage_base);
-  }
-  __syncthreads();
-  while (cur.ok) {
-    if (nxt.ok) stage_load(nxt);
-    // ---- compute on stage `cur`
+  int idx = 0;
+  if (s0.ok) issue(s0, 0);
+  if (s1.ok) issue(s1, 1);
+  while (s0.ok) {
+    // stage s0 (and the V tile) landed once only s1's loads may be pending
+    if (s1.ok) {
+      if (stat_wave) wait_vmcnt<C::SBPW + 1>();
+      else wait_vmcnt<C::SBPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_sync();
+    if (s2.ok) issue(s2, (idx + 2) % NS);
     {
-      const uint16_t* Qs = stage_base + buf * C::STAGE;
+      const uint16_t* Qs = stage_base + (idx % NS) * C::STAGE;
       const uint16_t* DOs = Qs + C::Q_ELEMS;
-      const uint16_t* QT = DOs + C::DO_ELEMS;
-      const uint16_t* DOT = QT + C::QT_ELEMS;
-      const float* stat = reinterpret_cast<const float*>(DOT + C::DOT_ELEMS);
-      const int svalid = cur.seg < 0 ? pr.P : resp_valid(pr, cur.seg);
-      const int s_posoff = cur.seg < 0 ? 0 : pr.P;
-      const int nrows = min(kStageRows, svalid - cur.r);
-      const int sq_lo = s_posoff + cur.r, sq_hi = sq_lo + nrows - 1;
+      const float* stat = reinterpret_cast<const float*>(DOs + C::DO_ELEMS);
+      const int s_posoff = s0.seg < 0 ? 0 : pr.P;
+      const int nrows = min(kStageRows, s0.svalid - s0.r);
+      const int sq_lo = s_posoff + s0.r, sq_hi = sq_lo + nrows - 1;
       // skip / full / masked for this wave's keys against the stage's queries
       int kind;
       if (wk_valid <= 0 || nrows <= 0 || sq_hi < wkp_lo || (pr.W > 0 && sq_lo - wkp_hi >= pr.W)) kind = 0;
@@ -447,10 +428,8 @@ __global__ void __launch_bounds__(NWK * 64)
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk) {
-          const int ro = l32 * C::QSTR + 16 * kk + 8 * hf;
-          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Vs + (wk0 + l32) * C::VSTR + 16 * kk + 8 * hf);
-          s = mfma32(*reinterpret_cast<const bf16x8*>(Qs + ro), kB[kk], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(DOs + ro), vb, dp);
+          s = mfma32(row_operand<D>(Qs, l32, kk, hf), kB[kk], s);
+          dp = mfma32(row_operand<D>(DOs, l32, kk, hf), row_operand<D>(Vs, wk0 + l32, kk, hf), dp);
         }
         bf16x8 pB[2], dsB[2];
         // query qc (+4*hf) of the stage is visible to this lane's key iff
@@ -467,7 +446,7 @@ __global__ void __launch_bounds__(NWK * 64)
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;                       // register index
             const int qc = 8 * g4 + e;                      // query row - 4*hf
-            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
+            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e] * kLog2e));
             if (kind == 2) {
               const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
               p = vis ? p : 0.f;
@@ -481,16 +460,15 @@ __global__ void __launch_bounds__(NWK * 64)
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            dVt[db] = mfma32(trans_read<kStageRows>(DOT, db * 32 + l32, ks, hf), pB[ks], dVt[db]);
-            dKt[db] = mfma32(trans_read<kStageRows>(QT, db * 32 + l32, ks, hf), dsB[ks], dKt[db]);
+            dVt[db] = mfma32(trans_operand<D>(DOs, 0, db * 32, ks, lane), pB[ks], dVt[db]);
+            dKt[db] = mfma32(trans_operand<D>(Qs, 0, db * 32, ks, lane), dsB[ks], dKt[db]);
           }
       }
     }
-    if (nxt.ok) stage_store(stage_base + (buf ^ 1) * C::STAGE);
-    __syncthreads();
-    cur = nxt;
-    if (nxt.ok) iter_next(pr, nxt, kp_lo, kp_hi);
-    buf ^= 1;
+    s0 = s1;
+    s1 = s2;
+    if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+    ++idx;
   }
 
   // ---- write dK (scaled) and dV for this lane's key
@@ -597,10 +575,10 @@ template <int D, int NW, int NWK, int kDqBN>
 hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, char* ws,
                hipStream_t stream) {
-  using CQ = DqCfg<D, kDqBN, NW>;
-  using CK = KvCfg<D, NWK>;
-  static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW>, CQ::LDS_BYTES);
-  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK>, CK::LDS_BYTES);
+  using CQ = DqCfg<D, kDqBN, NW, 3>;
+  using CK = KvCfg<D, NWK, 3>;
+  static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW, 3>, CQ::LDS_BYTES);
+  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, 3>, CK::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   const float* delta = reinterpret_cast<const float*>(ws + p.off_delta);
@@ -612,13 +590,13 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   const uint16_t* do16 = static_cast<const uint16_t*>(dout);
   hipError_t e;
   if (p.nwg_dq > 0) {
-    e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
+    e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW, 3>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
                stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
                static_cast<uint16_t*>(dq));
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
+    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, 3>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
                stream, pr, p.sh, q16, k16, v16, do16, lse, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;

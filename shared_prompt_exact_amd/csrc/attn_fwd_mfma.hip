@@ -26,7 +26,7 @@
 //    flight while tile i is computed, one barrier per tile;
 //  * workgroups are ordered longest key range first and remapped so each
 //    XCD runs a contiguous slice of that order (one KV head's K/V per L2).
-#include "tiles.h"
+#include "lds_tiles.h"
 
 namespace dualkv {
 namespace {
@@ -34,22 +34,24 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NS>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
-  static constexpr int KSTR = D + 8;               // padded K row (elements)
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int VT_ELEMS = D * BN;
-  static constexpr int STAGE = K_ELEMS + VT_ELEMS;  // elements per buffer
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int K_ELEMS = BN * D;            // swizzled row-major K tile
+  static constexpr int V_ELEMS = BN * D;            // swizzled row-major V tile
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;   // elements per ring slot
+  static constexpr int LDS_BYTES = NS * STAGE * 2;
+  static constexpr int KBLK = BN * D * 2 / 1024;    // 1 KiB blocks per K (or V) tile
+  static constexpr int BPW = KBLK / NW;             // blocks per wave per tile, for K and V each
+  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NS>
 __global__ void __launch_bounds__(NW * 64)
     fwd_mfma_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     uint16_t* __restrict__ o, float* __restrict__ lse) {
-  using C = FwdCfg<D, BN, NW>;
+  using C = FwdCfg<D, BN, NW, NS>;
   constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -84,6 +86,10 @@ __global__ void __launch_bounds__(NW * 64)
     if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf);
     qB[kk] = __builtin_bit_cast(bf16x8, z);
   }
+  // Q must be in registers before the key loop: the loop's own waits only
+  // count the tile loads, so drain it here (known to the compiler).
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
 
   f32x16 acc[DB];
 #pragma unroll
@@ -98,30 +104,32 @@ __global__ void __launch_bounds__(NW * 64)
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
     const int ntiles = tr.nA + tr.nB;
     const int64_t rs = (int64_t)pr.Hkv * D;
-    PairTile<BN, D, C::NT> kst, vst;
-    if (ntiles > 0) {
-      const KeyTile kt = tile_at(pr, b, tr, 0, BN);
+    // Ring of NS slots fed by direct global->LDS loads, NS-1 tiles ahead.
+    auto issue = [&](int t) {
+      const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
-      kst.load(k + off, rs, min(BN, kt.lim), tid);
-      vst.load(v + off, rs, min(BN, kt.lim), tid);
-      kst.store_rows(lds, tid);
-      vst.store_trans(lds + C::K_ELEMS, tid);
-    }
-    __syncthreads();
+      uint16_t* slot = lds + (t % NS) * C::STAGE;
+      const int nv = min(BN, kt.lim);
+      dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
+      dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < ntiles) issue(t);
 
     for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < ntiles) {
-        const KeyTile nx = tile_at(pr, b, tr, it + 1, BN);
-        const int64_t off = (int64_t)nx.row0 * rs + (int64_t)c * D;
-        kst.load(k + off, rs, min(BN, nx.lim), tid);
-        vst.load(v + off, rs, min(BN, nx.lim), tid);
-      }
+      // Tile `it` has landed once at most the loads of later issued tiles
+      // (up to NS-2 of them, 2*BPW instructions each) are pending.
+      if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
+      else wait_vmcnt<0>();
+      block_sync();
+      if (it + NS - 1 < ntiles) issue(it + NS - 1);
+
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
       if (kind != 0) {
-        const uint16_t* Ks = lds + cur * C::STAGE;
-        const uint16_t* Vt = Ks + C::K_ELEMS;
+        const uint16_t* Ks = lds + (it % NS) * C::STAGE;
+        const uint16_t* Vs = Ks + C::K_ELEMS;
         f32x16 s[NB32];
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
@@ -130,10 +138,8 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
-          for (int kb = 0; kb < NB32; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * C::KSTR + 16 * kk + 8 * hf);
-            s[kb] = mfma32(a, qB[kk], s[kb]);
-          }
+          for (int kb = 0; kb < NB32; ++kb)
+            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, kk, hf), qB[kk], s[kb]);
         if (kind == 2) {
           // Branch-free mask: key kc (+4*hf) is visible iff
           // 0 <= qpos - pos < window (one unsigned compare) and kc < lim.
@@ -158,11 +164,15 @@ __global__ void __launch_bounds__(NW * 64)
         const float muse = mnew == -INFINITY ? 0.f : mnew;
         const float alpha = __builtin_amdgcn_exp2f(m - muse);
         m = mnew;
-        l *= alpha;
+        // Rescale only when some row's running max moved (alpha == 1 exactly
+        // otherwise), which after the first tiles is the rare case.
+        if (__any(alpha != 1.f)) {
+          l *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
         bf16x8 pB[K16];
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
@@ -177,16 +187,9 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int ks = 0; ks < K16; ++ks) {
-            const bf16x8 a = trans_read<BN>(Vt, db * 32 + l32, ks, hf);
-            acc[db] = mfma32(a, pB[ks], acc[db]);
-          }
+          for (int ks = 0; ks < K16; ++ks)
+            acc[db] = mfma32(trans_operand<D>(Vs, 0, db * 32, ks, lane), pB[ks], acc[db]);
       }
-      if (it + 1 < ntiles) {
-        kst.store_rows(lds + (cur ^ 1) * C::STAGE, tid);
-        vst.store_trans(lds + (cur ^ 1) * C::STAGE + C::K_ELEMS, tid);
-      }
-      __syncthreads();
     }
   }
 
@@ -228,13 +231,13 @@ FwdPlan plan(const Problem& pr) {
   return p;
 }
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NS = 3>
 hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k, const void* v,
                void* o, float* lse, hipStream_t stream) {
-  using C = FwdCfg<D, BN, NW>;
-  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW>, C::LDS_BYTES);
+  using C = FwdCfg<D, BN, NW, NS>;
+  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW, NS>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  return launch("fwd", fwd_mfma_kernel<D, BN, NW>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
+  return launch("fwd", fwd_mfma_kernel<D, BN, NW, NS>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
                 stream, pr, p.HG, p.nbP, p.nbR, static_cast<const uint16_t*>(q),
                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                 static_cast<uint16_t*>(o), lse);

@@ -22,8 +22,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Exchange a value with the lane 32 positions away (the other half of the
-// wave): C-tile rows held by the two halves are disjoint.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// wave): C-tile rows held by the two halves are disjoint.  v_permlane32_swap
+// swaps the upper half of its first operand with the lower half of its
+// second, so with both set to x each lane finds its partner's value in the
+// result that its own half did not keep.
+__device__ __forceinline__ float swap_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // A C tile of 32 keys feeds the B operand of the next product in two
 // 16-key steps.  Register i of half h holds key 8*(i/4) + 4*h + i%4, so
