@@ -35,39 +35,45 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------- dq kernel
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS>
 struct DqCfg {
   static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
   static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int LDS_BYTES = NS * STAGE * 2;
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 32 * (BN / 32) * 4 : 0;   // partial S, dP
+  static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
   static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
   static constexpr int BPW = KBLK / NW;
   static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-template <int D, int BN, int NW, int NS>
+// DS = 2: a wave pair owns the same 32 query rows, each half of the head
+// dim (Q^T, dO^T, the contractions and the dQ accumulator); partial S and
+// dP meet in LDS and are summed in the same order by both waves.
+template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
     bwd_dq_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   const uint16_t* __restrict__ dout, const float* __restrict__ lse,
                   const float* __restrict__ delta, uint16_t* __restrict__ dq) {
-  using C = DqCfg<D, BN, NW, NS>;
+  using C = DqCfg<D, BN, NW, NS, DS>;
   constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
   extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BM = 32 * NW / HG;
+  const int dh = wave % DS, wq = wave / DS;
+  const int BM = 32 * NWQ / HG;
   const int NB = nbP + pr.N * nbR;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hgi = L / NB, blk = L % NB;
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
-  const int h = c * pr.g + (hgi % gpw) * HG + wave % HG;
+  const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
   const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
 
-  const int wr0 = b.r0 + (wave / HG) * 32;
+  const int wr0 = b.r0 + (wq / HG) * 32;
   const int my_r = wr0 + l32;
   const bool qvalid = my_r < b.nvalid;
   const int qpos = b.posoff + my_r;
@@ -78,12 +84,12 @@ __global__ void __launch_bounds__(NW * 64)
   const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
   const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
 
-  bf16x8 qB[KT], doB[KT];
+  bf16x8 qB[KTH], doB[KTH];
 #pragma unroll
-  for (int kk = 0; kk < KT; ++kk) {
+  for (int kk = 0; kk < KTH; ++kk) {
     uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (qvalid) {
-      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf;
+      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * (dh * KTH + kk) + 8 * hf;
       z = *reinterpret_cast<const uint4*>(q + off);
       y = *reinterpret_cast<const uint4*>(dout + off);
     }
@@ -101,11 +107,12 @@ __global__ void __launch_bounds__(NW * 64)
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
 
-  f32x16 acc[DB];
+  f32x16 acc[DBH];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBH; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float* const xch = reinterpret_cast<float*>(lds + NS * C::STAGE);   // DS > 1 only
 
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
@@ -129,21 +136,59 @@ __global__ void __launch_bounds__(NW * 64)
       if (it + NS - 1 < ntiles) issue(it + NS - 1);
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      const uint16_t* Ks = lds + (it % NS) * C::STAGE;
+      const uint16_t* Vs = Ks + C::K_ELEMS;
+      f32x16 s[NB32], dp[NB32];
+#pragma unroll
+      for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
       if (kind != 0) {
-        const uint16_t* Ks = lds + (it % NS) * C::STAGE;
-        const uint16_t* Vs = Ks + C::K_ELEMS;
-        f32x16 s[NB32], dp[NB32];
 #pragma unroll
-        for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
+        for (int kk = 0; kk < KTH; ++kk) {
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb) {
-            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, kk, hf), qB[kk], s[kb]);
-            dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, kk, hf), doB[kk], dp[kb]);
+            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
+            dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp[kb]);
           }
+          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (DS > 1) {
+        // partial S and dP of the DS waves sharing these rows meet in LDS;
+        // every wave adds the DS partials in index order (its own from
+        // registers), so all of them hold bit-identical sums
+        float* mine = xch + (wave * 64 + lane) * 32 * NB32;
+        if (kind != 0)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              *reinterpret_cast<float4*>(mine + 32 * kb + 4 * i4) =
+                  make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
+              *reinterpret_cast<float4*>(mine + 32 * kb + 16 + 4 * i4) =
+                  make_float4(dp[kb][4 * i4], dp[kb][4 * i4 + 1], dp[kb][4 * i4 + 2], dp[kb][4 * i4 + 3]);
+            }
+        block_sync();
+        if (kind != 0)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float ts = 0.f, td = 0.f;
+#pragma unroll
+              for (int pp = 0; pp < DS; ++pp) {
+                const float* o = xch + ((wave - dh + pp) * 64 + lane) * 32 * NB32 + 32 * kb;
+                const float vs = pp == dh ? s[kb][i] : o[i];
+                const float vd = pp == dh ? dp[kb][i] : o[16 + i];
+                ts = pp == 0 ? vs : ts + vs;
+                td = pp == 0 ? vd : td + vd;
+              }
+              s[kb][i] = ts;
+              dp[kb][i] = td;
+            }
+      }
+      if (kind != 0) {
         bf16x8 dsB[K16];
         const int d0 = qpos - kt.pos0 - 4 * hf;
         const int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
@@ -163,10 +208,12 @@ __global__ void __launch_bounds__(NW * 64)
               dsB[2 * kb + hs][j] = (__bf16)(p * (dp[kb][i] - dlt));
             }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBH; ++db) {
 #pragma unroll
           for (int ks = 0; ks < K16; ++ks)
-            acc[db] = mfma32(trans_operand<D>(Ks, 0, db * 32, ks, lane), dsB[ks], acc[db]);
+            acc[db] = mfma32(trans_operand<D>(Ks, 0, (dh * DBH + db) * 32, ks, lane), dsB[ks], acc[db]);
+          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -174,13 +221,13 @@ __global__ void __launch_bounds__(NW * 64)
   if (my_r < b.seglen) {
     uint16_t* orow = dq + qrow * ostride + (int64_t)h * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g4 + 4 * hf) = pk.u;
+        *reinterpret_cast<uint2*>(orow + (dh * DBH + db) * 32 + 8 * g4 + 4 * hf) = pk.u;
       }
   }
 }
@@ -189,15 +236,16 @@ __global__ void __launch_bounds__(NW * 64)
 
 constexpr int kStageRows = 32;
 
-template <int D, int NWK, int NS>
+template <int D, int NWK, int NS, int DS, bool VREG>
 struct KvCfg {
-  static constexpr int BK = 32 * NWK;               // keys per workgroup
-  static constexpr int V_ELEMS = BK * D;            // V tile (B operand of dP), loaded once
+  static constexpr int BK = 32 * NWK / DS;          // keys per workgroup
+  static constexpr int V_ELEMS = VREG ? 0 : BK * D; // V tile (B operand of dP), loaded once
   static constexpr int Q_ELEMS = kStageRows * D;    // Q stage rows
   static constexpr int DO_ELEMS = kStageRows * D;   // dO stage rows
   static constexpr int STAT = 2 * kStageRows * 2;   // LSE and delta, fp32 (in u16 units)
   static constexpr int STAGE = Q_ELEMS + DO_ELEMS + STAT;
-  static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2;
+  static constexpr int XCH_BYTES = DS > 1 ? NWK * 64 * 32 * 4 : 0;   // partial S, dP
+  static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2 + XCH_BYTES;
   static constexpr int VBPW = V_ELEMS * 2 / 1024 / NWK;     // V blocks per wave
   static constexpr int QBLK = Q_ELEMS * 2 / 1024;           // blocks per Q (or dO) stage tile
   static constexpr int SBPW = 2 * QBLK / NWK;               // stage blocks per wave
@@ -272,7 +320,11 @@ __device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int k
   iter_fix(pr, s, kp_lo, kp_hi);
 }
 
-template <int D, int NWK, int NS>
+// DS = 2: a wave pair owns the same 32 keys, each half of the head dim (K^T
+// and V^T operands, the S / dP contractions and the dK / dV accumulators);
+// partial S and dP meet in LDS.  VREG keeps V^T in registers instead of a
+// V tile in LDS (large head dims, where LDS is short).
+template <int D, int NWK, int NS, int DS, bool VREG>
 __global__ void __launch_bounds__(NWK * 64)
     bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -280,8 +332,8 @@ __global__ void __launch_bounds__(NWK * 64)
                     const float* __restrict__ delta, uint16_t* __restrict__ dk,
                     uint16_t* __restrict__ dv, float* __restrict__ part_k,
                     float* __restrict__ part_v) {
-  using C = KvCfg<D, NWK, NS>;
-  constexpr int KT = D / 16, DB = D / 32;
+  using C = KvCfg<D, NWK, NS, DS, VREG>;
+  constexpr int KT = D / 16, DB = D / 32, KTH = KT / DS, DBH = DB / DS;
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,32 +371,39 @@ __global__ void __launch_bounds__(NWK * 64)
   // ---- this wave's 32 keys: K^T as B operands in registers; the V tile
   // row-major in LDS (B operand of dP).  With K only in registers a wave
   // fits in 256 registers and two waves share each SIMD.
-  const int wk0 = 32 * wave;                          // first key of the wave in the tile
+  const int dh = wave % DS;                           // head-dim half of this wave
+  const int wk0 = 32 * (wave / DS);                   // first key of the wave in the tile
   const int my_k = wk0 + l32;
   const bool kvalid = my_k < klim;
   const int kpos = kp_lo + my_k;
   const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
   const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KT];
+  bf16x8 kB[KTH], vB[VREG ? KTH : 1];
 #pragma unroll
-  for (int kk = 0; kk < KT; ++kk) {
-    uint4 z = {0, 0, 0, 0};
-    if (kvalid) z = *reinterpret_cast<const uint4*>(k + krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf);
+  for (int kk = 0; kk < KTH; ++kk) {
+    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    const int64_t off = krow * kstride + (int64_t)c * D + 16 * (dh * KTH + kk) + 8 * hf;
+    if (kvalid) {
+      z = *reinterpret_cast<const uint4*>(k + off);
+      if constexpr (VREG) y = *reinterpret_cast<const uint4*>(v + off);
+    }
     kB[kk] = __builtin_bit_cast(bf16x8, z);
+    if constexpr (VREG) vB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   wait_vmcnt<0>();                    // the loop's waits count only LDS loads
   asm volatile("" ::: "memory");
   const uint16_t* Vs = lds;
   uint16_t* const stage_base = lds + C::V_ELEMS;
-  if (klim > 0)
+  if (!VREG && klim > 0)
     dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
                 min(C::BK, klim), lds, wave * C::VBPW, C::VBPW, lane);
+  float* const xch = reinterpret_cast<float*>(stage_base + NS * C::STAGE);   // DS > 1 only
   const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
-  f32x16 dKt[DB], dVt[DB];
+  f32x16 dKt[DBH], dVt[DBH];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBH; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dKt[db][i] = dVt[db][i] = 0.f;
 
@@ -365,9 +424,12 @@ __global__ void __launch_bounds__(NWK * 64)
   if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
   StageIter s1 = s0;
   if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
+  // NS == 3: stages s0, s1 in flight, s2 issued after the barrier;
+  // NS == 2: s0 in flight, s1 issued after the barrier;
+  // NS == 1: s1 issued once every wave is done with the single buffer.
+  static_assert(NS >= 1 && NS <= 3, "stage ring depth");
   StageIter s2 = s1;
-  if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
-  static_assert(NS == 3, "the ring below keeps two stages in flight");
+  if (NS == 3 && s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
 
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
@@ -398,17 +460,21 @@ __global__ void __launch_bounds__(NWK * 64)
 
   int idx = 0;
   if (s0.ok) issue(s0, 0);
-  if (s1.ok) issue(s1, 1);
+  if (NS == 3 && s1.ok) issue(s1, 1);
   while (s0.ok) {
     // stage s0 (and the V tile) landed once only s1's loads may be pending
-    if (s1.ok) {
+    if (NS == 3 && s1.ok) {
       if (stat_wave) wait_vmcnt<C::SBPW + 1>();
       else wait_vmcnt<C::SBPW>();
     } else {
       wait_vmcnt<0>();
     }
     block_sync();
-    if (s2.ok) issue(s2, (idx + 2) % NS);
+    if (NS == 3) {
+      if (s2.ok) issue(s2, (idx + 2) % NS);
+    } else if (NS == 2) {
+      if (s1.ok) issue(s1, (idx + 1) % NS);
+    }
     {
       const uint16_t* Qs = stage_base + (idx % NS) * C::STAGE;
       const uint16_t* DOs = Qs + C::Q_ELEMS;
@@ -422,15 +488,49 @@ __global__ void __launch_bounds__(NWK * 64)
       else if (wk_valid == 32 && nrows == kStageRows && sq_lo >= wkp_hi &&
                (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
       else kind = 2;
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
       if (kind != 0) {
-        f32x16 s, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
-          s = mfma32(row_operand<D>(Qs, l32, kk, hf), kB[kk], s);
-          dp = mfma32(row_operand<D>(DOs, l32, kk, hf), row_operand<D>(Vs, wk0 + l32, kk, hf), dp);
+        for (int kk = 0; kk < KTH; ++kk) {
+          const int kc = dh * KTH + kk;
+          const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + l32, kc, hf);
+          s = mfma32(row_operand<D>(Qs, l32, kc, hf), kB[kk], s);
+          dp = mfma32(row_operand<D>(DOs, l32, kc, hf), vb, dp);
+          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      if constexpr (DS > 1) {
+        // partial S and dP of the DS waves sharing these keys meet in LDS
+        // (all of them share `kind`); summed in index order by every wave
+        float* mine = xch + (wave * 64 + lane) * 32;
+        if (kind != 0)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            *reinterpret_cast<float4*>(mine + 4 * i4) =
+                make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+            *reinterpret_cast<float4*>(mine + 16 + 4 * i4) =
+                make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
+          }
+        block_sync();
+        if (kind != 0)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float ts = 0.f, td = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < DS; ++pp) {
+              const float* o = xch + ((wave - dh + pp) * 64 + lane) * 32;
+              const float vs = pp == dh ? s[i] : o[i];
+              const float vd = pp == dh ? dp[i] : o[16 + i];
+              ts = pp == 0 ? vs : ts + vs;
+              td = pp == 0 ? vd : td + vd;
+            }
+            s[i] = ts;
+            dp[i] = td;
+          }
+      }
+      if (kind != 0) {
         bf16x8 pB[2], dsB[2];
         // query qc (+4*hf) of the stage is visible to this lane's key iff
         // 0 <= qpos - kpos < window and qc < nrows (branch-free).
@@ -457,17 +557,28 @@ __global__ void __launch_bounds__(NWK * 64)
           }
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBH; ++db) {
+          const int col = (dh * DBH + db) * 32;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            dVt[db] = mfma32(trans_operand<D>(DOs, 0, db * 32, ks, lane), pB[ks], dVt[db]);
-            dKt[db] = mfma32(trans_operand<D>(Qs, 0, db * 32, ks, lane), dsB[ks], dKt[db]);
+            dVt[db] = mfma32(trans_operand<D>(DOs, 0, col, ks, lane), pB[ks], dVt[db]);
+            dKt[db] = mfma32(trans_operand<D>(Qs, 0, col, ks, lane), dsB[ks], dKt[db]);
           }
+          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
+    if (NS == 1) {
+      block_sync();                        // every wave is done with the buffer
+      if (s1.ok) issue(s1, 0);
+    }
     s0 = s1;
-    s1 = s2;
-    if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+    if (NS == 3) {
+      s1 = s2;
+      if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+    } else if (s1.ok) {
+      iter_next(pr, s1, kp_lo, kp_hi);
+    }
     ++idx;
   }
 
@@ -475,10 +586,10 @@ __global__ void __launch_bounds__(NWK * 64)
   if (my_k < seg_len - it.k0 && it.k0 + my_k < seg_len) {
     const bool partial = it.seg < 0 && sh.slots > 1;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hf;
+        const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
         if (partial) {
           const int64_t o = (((int64_t)it.slot * pr.P + it.k0 + my_k) * pr.Hkv + c) * D + d;
           *reinterpret_cast<float4*>(part_k + o) =
@@ -526,10 +637,16 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------------ planning
 
-constexpr int kNWK = 8;   // dK/dV waves per workgroup (2 per SIMD)
+// Waves per workgroup and head-dim split (DS waves share rows, each with
+// D/DS dims of state): dQ runs two waves per SIMD up to D = 256; dK/dV up to
+// D = 128; the rest one per SIMD.  D = 512 splits four ways.
+inline int dq_waves(int D) { return D <= 256 ? 8 : 4; }
+inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
+inline int dq_split(int D) { return D <= 128 ? 1 : (D <= 256 ? 2 : 4); }
+inline int kv_split(int D) { return D <= 128 ? 1 : (D <= 256 ? 2 : 4); }
 
 struct BwdPlan {
-  int NW, HG, BM, nbP, nbR;
+  int NW, DS, HG, BM, nbP, nbR;
   int64_t nwg_dq;
   KvShape sh;
   int64_t nwg_kv;
@@ -540,13 +657,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 BwdPlan plan(const Problem& pr) {
   BwdPlan p;
-  p.NW = 8;
-  p.HG = heads_per_block(pr.g, p.NW);
-  p.BM = 32 * p.NW / p.HG;
+  p.NW = dq_waves(pr.D);
+  p.DS = dq_split(pr.D);
+  p.HG = heads_per_block(pr.g, p.NW / p.DS);
+  p.BM = 32 * (p.NW / p.DS) / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
   p.nbR = (pr.R + p.BM - 1) / p.BM;
   p.nwg_dq = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
-  const int BK = 32 * kNWK;
+  const int BK = 32 * kv_waves(pr.D) / kv_split(pr.D);
   p.sh.nPt = (pr.P + BK - 1) / BK;
   p.sh.nRt = (pr.R + BK - 1) / BK;
   // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
@@ -571,14 +689,15 @@ BwdPlan plan(const Problem& pr) {
   return p;
 }
 
-template <int D, int NW, int NWK, int kDqBN>
+template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG>
 hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, char* ws,
                hipStream_t stream) {
-  using CQ = DqCfg<D, kDqBN, NW, 3>;
-  using CK = KvCfg<D, NWK, 3>;
-  static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW, 3>, CQ::LDS_BYTES);
-  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, 3>, CK::LDS_BYTES);
+  using CQ = DqCfg<D, kDqBN, NW, DQNS, DS>;
+  using CK = KvCfg<D, NWK, KVNS, KDS, VREG>;
+  static_assert(CQ::LDS_BYTES <= 160 * 1024 && CK::LDS_BYTES <= 160 * 1024, "LDS budget");
+  static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW, DQNS, DS>, CQ::LDS_BYTES);
+  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, CK::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   const float* delta = reinterpret_cast<const float*>(ws + p.off_delta);
@@ -590,13 +709,13 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   const uint16_t* do16 = static_cast<const uint16_t*>(dout);
   hipError_t e;
   if (p.nwg_dq > 0) {
-    e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW, 3>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
+    e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW, DQNS, DS>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
                stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
                static_cast<uint16_t*>(dq));
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, 3>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
+    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
                stream, pr, p.sh, q16, k16, v16, do16, lse, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
@@ -615,7 +734,7 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
 }  // namespace
 
 bool bwd_mfma_supported(const Problem& pr) {
-  if (pr.D != 64 && pr.D != 128) return false;
+  if (pr.D != 64 && pr.D != 128 && pr.D != 256 && pr.D != 512) return false;
   const BwdPlan p = plan(pr);
   return p.nwg_dq < ((int64_t)1 << 31) && p.nwg_kv < ((int64_t)1 << 31);
 }
@@ -631,8 +750,11 @@ hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, cons
                                   reinterpret_cast<float*>(ws + p.off_delta), stream);
   if (e != hipSuccess) return e;
   switch (pr.D) {
-    case 64: return run<64, 8, kNWK, 64>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, kNWK, 32>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    //                D  NW NWK BN DQNS KVNS DS KDS VREG
+    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 1, 4, 4, true>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,39 +34,46 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
   static constexpr int K_ELEMS = BN * D;            // swizzled row-major K tile
   static constexpr int V_ELEMS = BN * D;            // swizzled row-major V tile
   static constexpr int STAGE = K_ELEMS + V_ELEMS;   // elements per ring slot
-  static constexpr int LDS_BYTES = NS * STAGE * 2;
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 16 * 4 : 0;   // partial-score exchange
+  static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
   static constexpr int KBLK = BN * D * 2 / 1024;    // 1 KiB blocks per K (or V) tile
   static constexpr int BPW = KBLK / NW;             // blocks per wave per tile, for K and V each
   static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-template <int D, int BN, int NW, int NS>
+// DS = 2 splits the head dim over a pair of waves (waves 2j, 2j+1 own the
+// same 32 query rows, each half of D for Q^T, the K contraction and the O
+// accumulator); their partial scores meet in LDS, S = S_lo + S_hi, summed in
+// the same order by both so they agree bit for bit.
+template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
     fwd_mfma_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     uint16_t* __restrict__ o, float* __restrict__ lse) {
-  using C = FwdCfg<D, BN, NW, NS>;
+  using C = FwdCfg<D, BN, NW, NS, DS>;
   constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
   extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BM = 32 * NW / HG;
+  const int dh = wave % DS, wq = wave / DS;     // head-dim half, query slot
+  const int BM = 32 * NWQ / HG;
   const int NB = nbP + pr.N * nbR;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hgi = L / NB, blk = L % NB;
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
-  const int h = c * pr.g + (hgi % gpw) * HG + wave % HG;
+  const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
   const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
 
-  const int wr0 = b.r0 + (wave / HG) * 32;      // first row of this wave
+  const int wr0 = b.r0 + (wq / HG) * 32;        // first row of this wave
   const int my_r = wr0 + l32;
   const bool qvalid = my_r < b.nvalid;
   const int qpos = b.posoff + my_r;
@@ -78,12 +85,13 @@ __global__ void __launch_bounds__(NW * 64)
   const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
   const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
 
-  // Q^T as B operands, one per 16-wide head-dim step.
-  bf16x8 qB[KT];
+  // Q^T as B operands, one per 16-wide head-dim step of this wave's dims.
+  bf16x8 qB[KTH];
 #pragma unroll
-  for (int kk = 0; kk < KT; ++kk) {
+  for (int kk = 0; kk < KTH; ++kk) {
     uint4 z = {0, 0, 0, 0};
-    if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf);
+    if (qvalid)
+      z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * (dh * KTH + kk) + 8 * hf);
     qB[kk] = __builtin_bit_cast(bf16x8, z);
   }
   // Q must be in registers before the key loop: the loop's own waits only
@@ -91,12 +99,13 @@ __global__ void __launch_bounds__(NW * 64)
   wait_vmcnt<0>();
   asm volatile("" ::: "memory");
 
-  f32x16 acc[DB];
+  f32x16 acc[DBH];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBH; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m = -INFINITY, l = 0.f;
+  float* const xch = reinterpret_cast<float*>(lds + NS * C::STAGE);   // DS > 1 only
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;   // visible distance bound
 
@@ -127,19 +136,49 @@ __global__ void __launch_bounds__(NW * 64)
 
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      const uint16_t* Ks = lds + (it % NS) * C::STAGE;
+      const uint16_t* Vs = Ks + C::K_ELEMS;
+      f32x16 s[NB32];
+#pragma unroll
+      for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
       if (kind != 0) {
-        const uint16_t* Ks = lds + (it % NS) * C::STAGE;
-        const uint16_t* Vs = Ks + C::K_ELEMS;
-        f32x16 s[NB32];
 #pragma unroll
-        for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
+        for (int kk = 0; kk < KTH; ++kk) {
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb)
-            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, kk, hf), qB[kk], s[kb]);
+            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
+          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (DS > 1) {
+        // partial scores of the two halves meet in LDS (all waves pass the
+        // barrier; both members of a pair have the same `kind`)
+        float* mine = xch + (wave * 64 + lane) * 16 * NB32;
+        const float* other = xch + ((wave ^ 1) * 64 + lane) * 16 * NB32;
+        if (kind != 0)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              *reinterpret_cast<float4*>(mine + 16 * kb + 4 * i4) =
+                  make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
+        block_sync();
+        if (kind != 0)
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const float4 t = *reinterpret_cast<const float4*>(other + 16 * kb + 4 * i4);
+              // lower half first in both waves: identical sums
+              s[kb][4 * i4 + 0] = dh == 0 ? s[kb][4 * i4 + 0] + t.x : t.x + s[kb][4 * i4 + 0];
+              s[kb][4 * i4 + 1] = dh == 0 ? s[kb][4 * i4 + 1] + t.y : t.y + s[kb][4 * i4 + 1];
+              s[kb][4 * i4 + 2] = dh == 0 ? s[kb][4 * i4 + 2] + t.z : t.z + s[kb][4 * i4 + 2];
+              s[kb][4 * i4 + 3] = dh == 0 ? s[kb][4 * i4 + 3] + t.w : t.w + s[kb][4 * i4 + 3];
+            }
+      }
+      if (kind != 0) {
         if (kind == 2) {
           // Branch-free mask: key kc (+4*hf) is visible iff
           // 0 <= qpos - pos < window (one unsigned compare) and kc < lim.
@@ -169,7 +208,7 @@ __global__ void __launch_bounds__(NW * 64)
         if (__any(alpha != 1.f)) {
           l *= alpha;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DBH; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
         }
@@ -185,10 +224,12 @@ __global__ void __launch_bounds__(NW * 64)
               pB[2 * kb + hs][j] = (__bf16)p;
             }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBH; ++db) {
 #pragma unroll
           for (int ks = 0; ks < K16; ++ks)
-            acc[db] = mfma32(trans_operand<D>(Vs, 0, db * 32, ks, lane), pB[ks], acc[db]);
+            acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
+          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -200,44 +241,49 @@ __global__ void __launch_bounds__(NW * 64)
   if (my_r < b.seglen) {
     uint16_t* orow = o + qrow * ostride + (int64_t)h * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hf;
+        const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
         *reinterpret_cast<uint2*>(orow + d) = pk.u;
       }
-    if (hf == 0)
+    if (hf == 0 && dh == 0)
       lse[(int64_t)h * pr.T + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
 
 struct FwdPlan {
-  int NW, BN, HG, BM, nbP, nbR;
+  int NW, BN, DS, HG, BM, nbP, nbR;
   int64_t nwg;
 };
 
 FwdPlan plan(const Problem& pr) {
   FwdPlan p;
-  p.NW = pr.D <= 128 ? 8 : 4;
+  // Per wave, Q^T and the O accumulator take 3*D/4 registers: two waves per
+  // SIMD fit up to D = 128; D = 256 splits the head dim over wave pairs
+  // (still two per SIMD); D = 512 splits it and runs one wave per SIMD.
+  p.NW = pr.D <= 256 ? 8 : 4;
   p.BN = pr.D <= 128 ? 64 : 32;
-  p.HG = heads_per_block(pr.g, p.NW);
-  p.BM = 32 * p.NW / p.HG;
+  p.DS = pr.D <= 128 ? 1 : 2;
+  p.HG = heads_per_block(pr.g, p.NW / p.DS);
+  p.BM = 32 * (p.NW / p.DS) / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
   p.nbR = (pr.R + p.BM - 1) / p.BM;
   p.nwg = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
   return p;
 }
 
-template <int D, int BN, int NW, int NS = 3>
+template <int D, int BN, int NW, int NS, int DS>
 hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k, const void* v,
                void* o, float* lse, hipStream_t stream) {
-  using C = FwdCfg<D, BN, NW, NS>;
-  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW, NS>, C::LDS_BYTES);
+  using C = FwdCfg<D, BN, NW, NS, DS>;
+  static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  return launch("fwd", fwd_mfma_kernel<D, BN, NW, NS>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
+  return launch("fwd", fwd_mfma_kernel<D, BN, NW, NS, DS>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
                 stream, pr, p.HG, p.nbP, p.nbR, static_cast<const uint16_t*>(q),
                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                 static_cast<uint16_t*>(o), lse);
@@ -246,7 +292,7 @@ hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k
 }  // namespace
 
 bool fwd_mfma_supported(const Problem& pr) {
-  if (pr.D != 64 && pr.D != 128 && pr.D != 256) return false;
+  if (pr.D != 64 && pr.D != 128 && pr.D != 256 && pr.D != 512) return false;
   const FwdPlan p = plan(pr);
   return p.nwg < ((int64_t)1 << 31);
 }
@@ -256,9 +302,10 @@ hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, cons
   const FwdPlan p = plan(pr);
   if (p.nwg == 0) return hipSuccess;
   switch (pr.D) {
-    case 64: return run<64, 64, 8>(pr, p, q, k, v, o, lse, stream);
-    case 128: return run<128, 64, 8>(pr, p, q, k, v, o, lse, stream);
-    case 256: return run<256, 32, 4>(pr, p, q, k, v, o, lse, stream);
+    case 64: return run<64, 64, 8, 3, 1>(pr, p, q, k, v, o, lse, stream);
+    case 128: return run<128, 64, 8, 3, 1>(pr, p, q, k, v, o, lse, stream);
+    case 256: return run<256, 32, 8, 3, 2>(pr, p, q, k, v, o, lse, stream);
+    case 512: return run<512, 32, 4, 2, 2>(pr, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
 }

@@ -65,6 +65,10 @@ MID = [
     # GQA 8 (one 32-row slice per head in a block), head dim 256
     W("mid_gqa8", "bf16", 2, 100, 70, 8, 1, 128, 0, seed=27, value_scale=1.0),
     W("mid_d256", "bf16", 2, 90, 70, 4, 2, 256, 40, seed=28, value_scale=1.0),
+    # head dim 512 (head dim split over four waves) with GQA 4 and a ragged tail
+    W("mid_d512", "bf16", 3, 70, 45, 4, 1, 512, 0, seed=31, value_scale=1.0),
+    # head dim 256 without a window, valid lengths
+    W("mid_d256_valid", "bf16", 3, 100, 64, 8, 2, 256, 0, seed=32, value_scale=1.0, len_range=(1, 64)),
     # the benchmark value scale (0.5) at a reduced size
     W("mid_half", "bf16", 4, 256, 128, 8, 2, 128, 0, seed=29, value_scale=0.5),
 ]
@@ -80,7 +84,7 @@ def test_mid_cases_scalar_path(w):
     run_case(w, impl=dk.IMPL_SCALAR)
 
 
-@pytest.mark.parametrize("w", [m for m in MID if m.head_dim in (64, 128)], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", MID, ids=lambda w: w.name)
 def test_mid_cases_mfma_path(w):
     run_case(w, impl=dk.IMPL_MFMA)
 
