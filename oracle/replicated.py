@@ -25,6 +25,12 @@ Conventions as in ``oracle.dense`` (GQA h // g, natural-log LSE of scaled
 scores, empty rows O = 0 / LSE = -inf, padded rows masked as queries and
 keys, window W keeps 0 <= i - j < W).
 
+``delta_o="bf16"`` evaluates the backward as a function of a forward output
+stored in bfloat16: Delta = rowsum(dO * O) takes O rounded to bf16 (round
+to nearest, ties to even, via fp32), the value a bf16 forward hands to the
+backward; everything else stays fp64.  Used only to separate that rounding
+from kernel error on inputs where a near one-hot softmax amplifies it.
+
 TEST INFRASTRUCTURE ONLY.
 """
 from __future__ import annotations
@@ -32,8 +38,15 @@ from __future__ import annotations
 import numpy as np
 
 
+def round_bf16(x):
+    """fp64 -> fp32 -> bfloat16 (nearest, ties to even), returned as fp64."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def causal_sequence(q, k, v, do, n_valid, window=0, scale=None, chunk=1024,
-                    kv_heads=None, backward=True):
+                    kv_heads=None, backward=True, delta_o=None):
     """Standard causal attention on one sequence, forward and backward.
 
     q, do: [S, Hq, D]; k, v: [S, Hkv, D] (fp64).  Rows >= n_valid are
@@ -72,7 +85,8 @@ def causal_sequence(q, k, v, do, n_valid, window=0, scale=None, chunk=1024,
                 o[a:b, h, :] = o_c
                 lse[h, a:b] = lse_c
                 if backward:
-                    delta = (do[a:b, h, :] * o_c).sum(axis=1)
+                    o_d = round_bf16(o_c) if delta_o == "bf16" else o_c
+                    delta = (do[a:b, h, :] * o_d).sum(axis=1)
                     dp = do[a:b, h, :] @ v[:b, c, :].T
                     ds = p * (dp - delta[:, None])
                     dq[a:b, h, :] = scale * (ds @ k[:b, c, :])
@@ -87,7 +101,7 @@ def sequence_rows(n: int, N: int, P: int, R: int) -> np.ndarray:
 
 
 def replicated_fold(q, k, v, do, N, P, R, window=0, scale=None, valid_len=None,
-                    kv_heads=None, responses=None, chunk=1024, backward=True):
+                    kv_heads=None, responses=None, chunk=1024, backward=True, delta_o=None):
     """Packed-layout outputs computed through the N replicated sequences.
 
     q, do: packed [T, Hq, D]; k, v: packed [T, Hkv, D].  Returns dict(o,
@@ -119,7 +133,7 @@ def replicated_fold(q, k, v, do, N, P, R, window=0, scale=None, valid_len=None,
             if n != 0:
                 don[:P] = 0.0          # prompt dO belongs to copy 0 only
         res = causal_sequence(q[idx], k[idx], v[idx], don, P + L[n], window, scale,
-                              chunk, kv_heads, backward)
+                              chunk, kv_heads, backward, delta_o)
         rs = slice(P + n * R, P + (n + 1) * R)
         if first:
             out["o"][:P] = res["o"][:P]

@@ -385,3 +385,45 @@ def test_planted_mistake_window_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(replicated, "causal_sequence", mutated)
     with pytest.raises(AssertionError):
         test_zero_query_closed_form(2, 9, 6, 4, None)
+
+
+# ---------------------------------------------------------------- bf16 Delta variant
+
+def test_round_bf16_matches_torch():
+    """The oracle's own bf16 rounding equals torch's fp32 -> bfloat16 cast
+    (a library routine), ties and subnormals included."""
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -1 - 2 ** -8, 1e-40, -3e-39, 0.0, 65504.0])])
+    want = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(replicated.round_bf16(x), want)
+
+
+def test_bf16_delta_variant():
+    """delta_o='bf16' changes only Delta: the forward is identical; where O
+    is exact in bf16 (V rows all equal to a bf16 constant, so O = that row)
+    the backward is identical too; otherwise dQ moves by the predicted
+    amount scale * sum_j p_ij (Delta_i - Delta'_i) k_j."""
+    rng = np.random.default_rng(22)
+    N, P, R, Hq, Hkv, D = 2, 5, 4, 2, 1, 8
+    q, k, v, do = _rand(rng, P + N * R, Hq, Hkv, D)
+    a = replicated.replicated_fold(q, k, v, do, N, P, R)
+    b = replicated.replicated_fold(q, k, v, do, N, P, R, delta_o="bf16")
+    np.testing.assert_array_equal(a["o"], b["o"])
+    np.testing.assert_array_equal(a["lse"], b["lse"])
+    assert np.abs(a["dq"] - b["dq"]).max() > 0
+    c = replicated.round_bf16(rng.standard_normal(D))
+    vc = np.broadcast_to(c, v.shape).copy()
+    a = replicated.replicated_fold(q, k, vc, do, N, P, R)
+    b = replicated.replicated_fold(q, k, vc, do, N, P, R, delta_o="bf16")
+    for name in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(b[name], a[name], rtol=0, atol=1e-14)
+    # N = 1: dQ_i(bf16 Delta) - dQ_i = scale * (Delta_i - Delta'_i) * sum_j p_ij k_j
+    q1, k1, v1, do1 = q[:P + R], k[:P + R], v[:P + R], do[:P + R]
+    a = replicated.replicated_fold(q1, k1, v1, do1, 1, P, R)
+    b = replicated.replicated_fold(q1, k1, v1, do1, 1, P, R, delta_o="bf16")
+    ok = replicated.replicated_fold(q1, k1, k1, None, 1, P, R, backward=False)["o"]   # sum_j p_ij k_j
+    d_ex = (do1 * a["o"]).sum(-1)
+    d_bf = (do1 * replicated.round_bf16(a["o"])).sum(-1)
+    pred = (1 / np.sqrt(D)) * (d_ex - d_bf)[..., None] * ok
+    np.testing.assert_allclose(b["dq"] - a["dq"], pred, rtol=0, atol=1e-13)
