@@ -102,7 +102,7 @@ def main():
 
     import shared_prompt_exact_amd as dk
     import workloads
-    from shared_prompt_exact_amd import workcount
+    from shared_prompt_exact_amd import profiling, workcount
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -167,9 +167,13 @@ def main():
             kernels[name]["tflops"] = kf / (kernels[name]["avg_ms"] * 1e-3) / 1e12
     dom = max(kernel_flops, key=lambda n: kernels.get(n, {"avg_ms": 0})["avg_ms"] * kernels.get(n, {"launches": 0})["launches"])
     dom_ach = kernels[dom]["tflops"]
+    # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    # record of this kernel and workload; null once its sources have changed.
+    trec = profiling.load_traffic(dom, w.name)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_ach, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(dom_ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None if trec is None else trec["bytes_per_launch"]}
 
     # Repack of hidden-state-sized rows (Hq*D bf16 per token), HBM bound.
     rep_rows = dk.dualkv_repack(do, N, P, R, dk.DUALKV_SCATTER)

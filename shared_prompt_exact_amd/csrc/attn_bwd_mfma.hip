@@ -33,6 +33,16 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+// Ring slot of a tile: a compile-time constant (IntC) on the unrolled path,
+// a runtime value otherwise.
+template <int V>
+__device__ __forceinline__ constexpr int slot_value(IntC<V>) { return V; }
+__device__ __forceinline__ int slot_value(int x) { return x; }
+
 // ----------------------------------------------------------------- dq kernel
 
 template <int D, int BN, int NW, int NS, int DS>
@@ -129,14 +139,18 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)
       if (t < ntiles) issue(t);
-    for (int it = 0; it < ntiles; ++it) {
+    // One key tile.  Where the loop below is unrolled by NS the ring slot is
+    // a compile-time constant, so LDS addresses are per-lane bases plus
+    // immediates.
+    auto step = [&](int it, auto slot_c) {
+      const int SLOT = slot_value(slot_c);
       if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
       else wait_vmcnt<0>();
       block_sync();
       if (it + NS - 1 < ntiles) issue(it + NS - 1);
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
-      const uint16_t* Ks = lds + (it % NS) * C::STAGE;
+      const uint16_t* Ks = lds + SLOT * C::STAGE;
       const uint16_t* Vs = Ks + C::K_ELEMS;
       f32x16 s[NB32], dp[NB32];
 #pragma unroll
@@ -215,6 +229,20 @@ __global__ void __launch_bounds__(NW * 64)
           if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    static_assert(NS == 2 || NS == 3, "ring depth");
+    if constexpr (D <= 128) {
+      // unrolled by the ring depth (small head dims: registers to spare)
+      int it = 0;
+      for (; it + NS <= ntiles; it += NS) {
+        step(it, IntC<0>{});
+        step(it + 1, IntC<1>{});
+        if constexpr (NS == 3) step(it + 2, IntC<2>{});
+      }
+      if (it < ntiles) step(it, IntC<0>{});
+      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+    } else {
+      for (int it = 0; it < ntiles; ++it) step(it, it % NS);
     }
   }
 

@@ -18,12 +18,15 @@
 //    row max needs one exchange between wave halves, its row sum none
 //    until the end, and the S^T accumulator becomes the B operand of
 //    O^T += V^T P^T without any data movement;
-//  * Q^T stays in registers for the whole key loop; K tiles sit row-major
-//    in LDS (padded rows, conflict-free 128-bit reads); V tiles are
-//    transposed in registers on their way into LDS, in the perm16 key order
-//    with an XOR chunk swizzle;
-//  * K/V tiles are double buffered: the global loads of tile i+1 are in
-//    flight while tile i is computed, one barrier per tile;
+//  * Q^T stays in registers for the whole key loop; K and V tiles sit
+//    row-major in LDS (XOR-swizzled 16-byte chunks), K read as row
+//    operands, V as transposed operands (ds_read_b64_tr_b16), both free of
+//    bank conflicts;
+//  * tiles arrive by direct global->LDS loads into a ring of NS slots, NS-1
+//    tiles ahead, one barrier per tile; the loop is unrolled by NS so every
+//    LDS address is a per-lane base plus an immediate;
+//  * the O rescale runs only when a row's running max grows by more than
+//    2^8 (the softmax is exact for any reference max);
 //  * workgroups are ordered longest key range first and remapped so each
 //    XCD runs a contiguous slice of that order (one KV head's K/V per L2).
 #include "lds_tiles.h"
@@ -33,6 +36,17 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescale = 8.f;   // log2 units: p <= 256 between rescales
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+// Ring slot of a tile: a compile-time constant (IntC) on the unrolled path,
+// a runtime value otherwise.
+template <int V>
+__device__ __forceinline__ constexpr int slot_value(IntC<V>) { return V; }
+__device__ __forceinline__ int slot_value(int x) { return x; }
 
 template <int D, int BN, int NW, int NS, int DS>
 struct FwdCfg {
@@ -126,7 +140,11 @@ __global__ void __launch_bounds__(NW * 64)
     for (int t = 0; t < NS - 1; ++t)
       if (t < ntiles) issue(t);
 
-    for (int it = 0; it < ntiles; ++it) {
+    // One key tile.  Where the loop below is unrolled by NS the ring slot is
+    // a compile-time constant, so every LDS operand address is a per-lane
+    // base plus an immediate offset.
+    auto step = [&](int it, auto slot_c) {
+      const int SLOT = slot_value(slot_c);
       // Tile `it` has landed once at most the loads of later issued tiles
       // (up to NS-2 of them, 2*BPW instructions each) are pending.
       if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
@@ -136,7 +154,7 @@ __global__ void __launch_bounds__(NW * 64)
 
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
-      const uint16_t* Ks = lds + (it % NS) * C::STAGE;
+      const uint16_t* Ks = lds + SLOT * C::STAGE;
       const uint16_t* Vs = Ks + C::K_ELEMS;
       f32x16 s[NB32];
 #pragma unroll
@@ -199,19 +217,23 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         mx = fmaxf(mx, swap_halves(mx));
-        const float mnew = fmaxf(m, mx * c2);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - muse);
-        m = mnew;
-        // Rescale only when some row's running max moved (alpha == 1 exactly
-        // otherwise), which after the first tiles is the rare case.
-        if (__any(alpha != 1.f)) {
+        // The running max m only moves when the tile's max exceeds it by
+        // more than kRescale (log2 units): the softmax is the same for any
+        // reference value (numerator and denominator share it), p stays
+        // below 2^kRescale, and the O rescale -- a multiply per accumulator
+        // register -- becomes rare instead of happening on most tiles.
+        const bool grow = mx * c2 > m + kRescale;
+        if (__any(grow)) {
+          const float mnew = grow ? mx * c2 : m;
+          const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+          m = mnew;
           l *= alpha;
 #pragma unroll
           for (int db = 0; db < DBH; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
         }
+        const float muse = m == -INFINITY ? 0.f : m;   // rows with no key yet: p = 0
         bf16x8 pB[K16];
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
@@ -231,6 +253,20 @@ __global__ void __launch_bounds__(NW * 64)
           if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    static_assert(NS == 2 || NS == 3, "ring depth");
+    if constexpr (D <= 128) {
+      // unrolled by the ring depth (small head dims: registers to spare)
+      int it = 0;
+      for (; it + NS <= ntiles; it += NS) {
+        step(it, IntC<0>{});
+        step(it + 1, IntC<1>{});
+        if constexpr (NS == 3) step(it + 2, IntC<2>{});
+      }
+      if (it < ntiles) step(it, IntC<0>{});
+      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+    } else {
+      for (int it = 0; it < ntiles; ++it) step(it, it % NS);
     }
   }
 

@@ -2,14 +2,19 @@
 //
 // A tile holds ROWS packed rows of one head (D bf16 each) row-major in
 // LDS, 16-byte chunks XOR-swizzled per row: logical chunk c of row r sits
-// at chunk c ^ swz(r).  One swizzle serves both operand reads:
-//  * row operands (128-bit ds_read, 8 consecutive rows at one logical
-//    chunk): swz over 8 consecutive rows takes 8 distinct values, so the
-//    rows spread over all banks;
-//  * transposed operands (ds_read_b64_tr_b16: a 16-lane group reads 4
-//    consecutive rows x 32 bytes): swz/2 differs across the 4 rows, so the
-//    8 chunks read are distinct.
-//
+// at chunk c ^ swz<D>(r).  gfx950's LDS serves 256 bytes per clock over 64
+// four-byte banks, so an access is conflict free when the 16-byte chunks
+// that one clock serves land on 16 distinct positions modulo 256 bytes.
+// One swizzle serves both operand reads:
+//  * row operands (128-bit ds_read, 16 lanes per clock = 16 consecutive
+//    rows at one logical chunk): swz takes 16 distinct values over 16
+//    consecutive rows (D >= 128; rows are 256 B or more, so the position is
+//    the chunk index mod 16), or 8 distinct values over the 8 rows of each
+//    parity (D = 64: two 128-byte rows per 256 bytes);
+//  * transposed operands (ds_read_b64_tr_b16, 32 lanes per clock = 4
+//    consecutive rows x 4 consecutive chunks): the 4 rows differ in swz
+//    bits 2-3 (D = 64: the two rows of each parity differ in bit 2), the 4
+//    chunks in bits 0-1, so the 16 chunks read are distinct.
 // Loading: global_load_lds_dwordx4 writes 64 lanes x 16 bytes = 1 KiB of
 // LDS at a wave-uniform base, lane i at base + 16*i.  Lane i therefore
 // fetches the global chunk that belongs at physical chunk i of its row.
@@ -30,12 +35,16 @@ typedef short lds_short4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) lds_short4 lds_short4_as3;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return ((row & 3) << 2) | ((row >> 2) & 3);
+}
 
 // Element offset of (row, col) in a swizzled tile with D columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
 }
 
 // Wait until at most N vector-memory operations of this wave are pending.
@@ -72,7 +81,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ g, int64_t
     const int blk = first_block + b;
     const int row = blk * RPB + lane / CPR;
     const int p = lane % CPR;
-    const int c = p ^ swz(row);
+    const int c = p ^ swz<D>(row);
     const int src = row < nvalid ? row : nvalid - 1;
     const uint16_t* gp = g + (int64_t)src * rs + c * 8;
     // LDS base of the block in M0 (wave-uniform), 16 bytes per lane.
@@ -85,7 +94,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ g, int64_t
 // Row operand: row `row`, k-step kk (16 columns), wave half hf.
 template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int row, int kk, int hf) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * D + (((2 * kk + hf) ^ swz(row)) << 3));
+  return *reinterpret_cast<const bf16x8*>(tile + row * D + (((2 * kk + hf) ^ swz<D>(row)) << 3));
 }
 
 // Transposed operand for v_mfma_f32_32x32x16_bf16: A[i][k] = tile[row0 + k][col0 + i]
