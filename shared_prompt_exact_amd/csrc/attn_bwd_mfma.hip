@@ -204,8 +204,20 @@ __global__ void __launch_bounds__(NW * 64)
       }
       if (kind != 0) {
         bf16x8 dsB[K16];
-        const int d0 = qpos - kt.pos0 - 4 * hf;
-        const int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
+        if (kind == 2) {
+          // hidden scores become -inf: p = exp2(-inf - lse2) = 0 below
+          int d0 = qpos - kt.pos0 - 4 * hf;
+          int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
+          asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+              s[kb][i] = vis ? s[kb][i] : -INFINITY;
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
@@ -213,12 +225,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int i = 8 * hs + j;
-              float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
-              if (kind == 2) {   // branch-free mask (see the forward)
-                const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
-                const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
-                p = vis ? p : 0.f;
-              }
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
               dsB[2 * kb + hs][j] = (__bf16)(p * (dp[kb][i] - dlt));
             }
 #pragma unroll
@@ -356,7 +363,7 @@ template <int D, int NWK, int NS, int DS, bool VREG>
 __global__ void __launch_bounds__(NWK * 64)
     bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                    const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk,
                     uint16_t* __restrict__ dv, float* __restrict__ part_k,
                     float* __restrict__ part_v) {
@@ -462,7 +469,7 @@ __global__ void __launch_bounds__(NWK * 64)
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
-  const bool stat_wave = wave == NWK - 1;    // also loads the stage's LSE / delta
+  const bool stat_wave = wave == NWK - 1;    // also loads the stage's lse2 / delta
 
   auto issue = [&](const StageIter& st, int slot) {
     const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
@@ -477,9 +484,9 @@ __global__ void __launch_bounds__(NWK * 64)
       else dma_rows<D>(dout + off, qstride, n, buf + C::Q_ELEMS, blk - C::QBLK, 1, lane);
     }
     if (stat_wave) {
-      // 64 lanes x 4 bytes: LSE of the 32 rows, then their delta
+      // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
       const int row = sb + st.r + min(lane & 31, n - 1);
-      const float* src = (lane < 32 ? lse : delta) + (int64_t)st.h * pr.T + row;
+      const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.T + row;
       const unsigned ldsaddr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
           __attribute__((address_space(3))) void*)(buf + C::Q_ELEMS + C::DO_ELEMS));
       asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
@@ -560,10 +567,20 @@ __global__ void __launch_bounds__(NWK * 64)
       }
       if (kind != 0) {
         bf16x8 pB[2], dsB[2];
-        // query qc (+4*hf) of the stage is visible to this lane's key iff
-        // 0 <= qpos - kpos < window and qc < nrows (branch-free).
-        const int e0 = sq_lo + 4 * hf - kpos;
-        const int n0 = (kvalid ? nrows : 0) - 4 * hf;
+        if (kind == 2) {
+          // query qc (+4*hf) of the stage is visible to this lane's key iff
+          // 0 <= qpos - kpos < window and qc < nrows (branch-free); hidden
+          // scores become -inf, so p = exp2(-inf - lse2) = 0 below.
+          int e0 = sq_lo + 4 * hf - kpos;
+          int n0 = (kvalid ? nrows : 0) - 4 * hf;
+          asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qc = 8 * (i >> 2) + (i & 3);           // query row - 4*hf
+            const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
+            s[i] = vis ? s[i] : -INFINITY;
+          }
+        }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * g4 + 4 * hf);
@@ -573,12 +590,7 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;                       // register index
-            const int qc = 8 * g4 + e;                      // query row - 4*hf
-            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e] * kLog2e));
-            if (kind == 2) {
-              const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
-              p = vis ? p : 0.f;
-            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
             const float ds = p * (dp[i] - dv4[e]);
             pB[i >> 3][i & 7] = (__bf16)p;
             dsB[i >> 3][i & 7] = (__bf16)ds;
@@ -640,6 +652,47 @@ __global__ void __launch_bounds__(NWK * 64)
   }
 }
 
+// ------------------------------------------------------------- preprocess
+//
+// Per query row and head: Delta = sum_d dO * O (fp32) and lse2 = LSE * log2(e)
+// (+inf on rows without a visible key, so exp2(s*c - lse2) is 0 there for
+// any finite or -inf score).  D/8 lanes share a row, 16 bytes of O and dO
+// each, so a wave reads 1 KiB contiguous per operand; rows are the packed
+// [T, Hq] order of O.
+__device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+template <int D>
+__global__ void __launch_bounds__(256)
+    delta_lse2_kernel(Problem pr, const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                      const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ lse2) {
+  constexpr int G = D / 8;                  // lanes per row
+  constexpr int RPW = 64 / G;               // rows per wave
+  const int lane = threadIdx.x & 63, sub = lane % G;
+  const int64_t nrows = (int64_t)pr.T * pr.Hq;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+  float acc = 0.f;
+  if (row < nrows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + 8 * sub);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + 8 * sub);
+    const unsigned av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(bf16_lo(av[j]), bf16_lo(bv[j]), acc);
+      acc = fmaf(bf16_hi(av[j]), bf16_hi(bv[j]), acc);
+    }
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < nrows && sub == 0) {
+    const int t = (int)(row / pr.Hq), h = (int)(row % pr.Hq);
+    const int64_t at = (int64_t)h * pr.T + t;
+    const float L = lse[at];
+    delta[at] = L == -INFINITY ? 0.f : acc;
+    lse2[at] = L == -INFINITY ? INFINITY : L * kLog2e;
+  }
+}
+
 // ------------------------------------------------------------ slot reduction
 
 __global__ void __launch_bounds__(256)
@@ -678,7 +731,7 @@ struct BwdPlan {
   int64_t nwg_dq;
   KvShape sh;
   int64_t nwg_kv;
-  size_t off_delta, off_pk, off_pv, bytes;
+  size_t off_delta, off_lse2, off_pk, off_pv, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -709,8 +762,8 @@ BwdPlan plan(const Problem& pr) {
   p.sh.slots = 1 + rslots;
   p.nwg_kv = ((int64_t)p.sh.nPt * p.sh.slots + (int64_t)pr.N * p.sh.nRt) * pr.Hkv;
   p.off_delta = 0;
-  size_t b = align256((size_t)pr.Hq * pr.T * sizeof(float));
-  p.off_pk = b;
+  p.off_lse2 = align256((size_t)pr.Hq * pr.T * sizeof(float));
+  p.off_pk = 2 * p.off_lse2;
   const size_t part = p.sh.slots > 1 ? align256((size_t)p.sh.slots * pr.P * pr.Hkv * pr.D * sizeof(float)) : 0;
   p.off_pv = p.off_pk + part;
   p.bytes = p.off_pv + part;
@@ -719,8 +772,8 @@ BwdPlan plan(const Problem& pr) {
 
 template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG>
 hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
-               const float* lse, const void* dout, void* dq, void* dk, void* dv, char* ws,
-               hipStream_t stream) {
+               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               char* ws, hipStream_t stream) {
   using CQ = DqCfg<D, kDqBN, NW, DQNS, DS>;
   using CK = KvCfg<D, NWK, KVNS, KDS, VREG>;
   static_assert(CQ::LDS_BYTES <= 160 * 1024 && CK::LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -728,7 +781,8 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, CK::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
-  const float* delta = reinterpret_cast<const float*>(ws + p.off_delta);
+  float* delta = reinterpret_cast<float*>(ws + p.off_delta);
+  float* lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
   float* pk = reinterpret_cast<float*>(ws + p.off_pk);
   float* pv = reinterpret_cast<float*>(ws + p.off_pv);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
@@ -736,6 +790,13 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const uint16_t* do16 = static_cast<const uint16_t*>(dout);
   hipError_t e;
+  {
+    constexpr int RPB = 4 * 64 / (D / 8);   // rows per 256-thread block
+    const int64_t nrows = (int64_t)pr.T * pr.Hq;
+    e = launch("bwd_delta", delta_lse2_kernel<D>, dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0,
+               stream, pr, static_cast<const uint16_t*>(o), do16, lse, delta, lse2);
+    if (e != hipSuccess) return e;
+  }
   if (p.nwg_dq > 0) {
     e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW, DQNS, DS>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
                stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
@@ -744,7 +805,7 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   }
   if (p.nwg_kv > 0) {
     e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
-               stream, pr, p.sh, q16, k16, v16, do16, lse, delta, static_cast<uint16_t*>(dk),
+               stream, pr, p.sh, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
   }
@@ -774,15 +835,12 @@ hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, cons
                            void* dv, void* workspace, hipStream_t stream) {
   const BwdPlan p = plan(pr);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = launch_bwd_delta(pr, DUALKV_BF16, o, dout, lse,
-                                  reinterpret_cast<float*>(ws + p.off_delta), stream);
-  if (e != hipSuccess) return e;
   switch (pr.D) {
     //                D  NW NWK BN DQNS KVNS DS KDS VREG
-    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 1, 4, 4, true>(pr, p, q, k, v, lse, dout, dq, dk, dv, ws, stream);
+    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 1, 4, 4, true>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
