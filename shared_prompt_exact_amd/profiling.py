@@ -38,7 +38,7 @@ KERNELS = {
     "bwd_dq": ("bwd_dq_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_dkdv": ("bwd_dkdv_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_reduce": ("reduce_slots_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
-    "bwd_delta": ("delta_kernel", ["attn_scalar.hip"] + _HEADERS),
+    "bwd_delta": ("delta_lse2_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "repack": ("repack_kernel", ["repack.hip", "common.h"]),
 }
 
