@@ -23,6 +23,9 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     # keep the compiler from forming packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs (accumulation registers then serve as
+    # overflow): the head-dim-split kernels stop spilling to scratch
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

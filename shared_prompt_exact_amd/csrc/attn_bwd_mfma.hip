@@ -172,15 +172,19 @@ __global__ void __launch_bounds__(NW * 64)
         // partial S and dP of the DS waves sharing these rows meet in LDS;
         // every wave adds the DS partials in index order (its own from
         // registers), so all of them hold bit-identical sums
-        float* mine = xch + (wave * 64 + lane) * 32 * NB32;
+        // layout [wave][float4 j][lane] (S in j = 8kb .. 8kb+3, dP in
+        // 8kb+4 .. 8kb+7): each 16-byte access of a wave covers 1 KiB
+        // contiguous (no bank conflicts)
+        float4* const x4 = reinterpret_cast<float4*>(xch);
+        constexpr int J = 8 * NB32;
         if (kind != 0)
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              *reinterpret_cast<float4*>(mine + 32 * kb + 4 * i4) =
+              x4[(wave * J + 8 * kb + i4) * 64 + lane] =
                   make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
-              *reinterpret_cast<float4*>(mine + 32 * kb + 16 + 4 * i4) =
+              x4[(wave * J + 8 * kb + 4 + i4) * 64 + lane] =
                   make_float4(dp[kb][4 * i4], dp[kb][4 * i4 + 1], dp[kb][4 * i4 + 2], dp[kb][4 * i4 + 3]);
             }
         block_sync();
@@ -188,18 +192,25 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float ts = 0.f, td = 0.f;
+            for (int i4 = 0; i4 < 4; ++i4) {
+              float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
 #pragma unroll
               for (int pp = 0; pp < DS; ++pp) {
-                const float* o = xch + ((wave - dh + pp) * 64 + lane) * 32 * NB32 + 32 * kb;
-                const float vs = pp == dh ? s[kb][i] : o[i];
-                const float vd = pp == dh ? dp[kb][i] : o[16 + i];
-                ts = pp == 0 ? vs : ts + vs;
-                td = pp == 0 ? vd : td + vd;
+                const int w = wave - dh + pp;
+                const float4 vs = pp == dh ? make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3])
+                                           : x4[(w * J + 8 * kb + i4) * 64 + lane];
+                const float4 vd = pp == dh ? make_float4(dp[kb][4 * i4], dp[kb][4 * i4 + 1], dp[kb][4 * i4 + 2], dp[kb][4 * i4 + 3])
+                                           : x4[(w * J + 8 * kb + 4 + i4) * 64 + lane];
+                if (pp == 0) {
+                  ts4 = vs;
+                  td4 = vd;
+                } else {
+                  ts4.x += vs.x; ts4.y += vs.y; ts4.z += vs.z; ts4.w += vs.w;
+                  td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
+                }
               }
-              s[kb][i] = ts;
-              dp[kb][i] = td;
+              s[kb][4 * i4] = ts4.x; s[kb][4 * i4 + 1] = ts4.y; s[kb][4 * i4 + 2] = ts4.z; s[kb][4 * i4 + 3] = ts4.w;
+              dp[kb][4 * i4] = td4.x; dp[kb][4 * i4 + 1] = td4.y; dp[kb][4 * i4 + 2] = td4.z; dp[kb][4 * i4 + 3] = td4.w;
             }
       }
       if (kind != 0) {
@@ -271,9 +282,9 @@ __global__ void __launch_bounds__(NW * 64)
 
 constexpr int kStageRows = 32;
 
-template <int D, int NWK, int NS, int DS, bool VREG>
+template <int D, int NWK, int NS, int DS, bool VREG, int KW>
 struct KvCfg {
-  static constexpr int BK = 32 * NWK / DS;          // keys per workgroup
+  static constexpr int BK = 32 * KW * NWK / DS;     // keys per workgroup
   static constexpr int V_ELEMS = VREG ? 0 : BK * D; // V tile (B operand of dP), loaded once
   static constexpr int Q_ELEMS = kStageRows * D;    // Q stage rows
   static constexpr int DO_ELEMS = kStageRows * D;   // dO stage rows
@@ -358,17 +369,21 @@ __device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int k
 // DS = 2: a wave pair owns the same 32 keys, each half of the head dim (K^T
 // and V^T operands, the S / dP contractions and the dK / dV accumulators);
 // partial S and dP meet in LDS.  VREG keeps V^T in registers instead of a
-// V tile in LDS (large head dims, where LDS is short).
-template <int D, int NWK, int NS, int DS, bool VREG>
-__global__ void __launch_bounds__(NWK * 64)
+// V tile in LDS (large head dims, where LDS is short).  KW = 2: a wave owns
+// two 32-key tiles (one wave per SIMD, the dK / dV accumulators in the
+// accumulation registers), so each Q, dO, Q^T, dO^T operand read from LDS
+// feeds two MFMAs.
+template <int D, int NWK, int NS, int DS, bool VREG, int KW>
+__global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, KW == 2 ? 1 : 8)))
     bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk,
                     uint16_t* __restrict__ dv, float* __restrict__ part_k,
                     float* __restrict__ part_v) {
-  using C = KvCfg<D, NWK, NS, DS, VREG>;
+  using C = KvCfg<D, NWK, NS, DS, VREG, KW>;
   constexpr int KT = D / 16, DB = D / 32, KTH = KT / DS, DBH = DB / DS;
+  static_assert(KW == 1 || (DS == 1 && !VREG), "two key tiles per wave: no head-dim split");
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -403,27 +418,33 @@ __global__ void __launch_bounds__(NWK * 64)
   const int kp_lo = posoff + it.k0;
   const int kp_hi = posoff + it.k0 + min(C::BK, max(klim, 1)) - 1;
 
-  // ---- this wave's 32 keys: K^T as B operands in registers; the V tile
-  // row-major in LDS (B operand of dP).  With K only in registers a wave
-  // fits in 256 registers and two waves share each SIMD.
+  // ---- this wave's 32*KW keys: K^T as B operands in registers; the V
+  // tile row-major in LDS (B operand of dP).  With K only in registers a
+  // wave of one key tile fits in 256 registers and two waves share each SIMD.
   const int dh = wave % DS;                           // head-dim half of this wave
-  const int wk0 = 32 * (wave / DS);                   // first key of the wave in the tile
-  const int my_k = wk0 + l32;
-  const bool kvalid = my_k < klim;
-  const int kpos = kp_lo + my_k;
-  const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
+  const int wk0 = 32 * KW * (wave / DS);              // first key of the wave in the tile
+  int my_k[KW], kpos[KW];
+  bool kvalid[KW];
+  int64_t krow[KW];
   const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KTH], vB[VREG ? KTH : 1];
+  bf16x8 kB[KW][KTH], vB[VREG ? KTH : 1];
 #pragma unroll
-  for (int kk = 0; kk < KTH; ++kk) {
-    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    const int64_t off = krow * kstride + (int64_t)c * D + 16 * (dh * KTH + kk) + 8 * hf;
-    if (kvalid) {
-      z = *reinterpret_cast<const uint4*>(k + off);
-      if constexpr (VREG) y = *reinterpret_cast<const uint4*>(v + off);
+  for (int kt = 0; kt < KW; ++kt) {
+    my_k[kt] = wk0 + 32 * kt + l32;
+    kvalid[kt] = my_k[kt] < klim;
+    kpos[kt] = kp_lo + my_k[kt];
+    krow[kt] = (int64_t)seg_base + it.k0 + my_k[kt];
+#pragma unroll
+    for (int kk = 0; kk < KTH; ++kk) {
+      uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+      const int64_t off = krow[kt] * kstride + (int64_t)c * D + 16 * (dh * KTH + kk) + 8 * hf;
+      if (kvalid[kt]) {
+        z = *reinterpret_cast<const uint4*>(k + off);
+        if constexpr (VREG) y = *reinterpret_cast<const uint4*>(v + off);
+      }
+      kB[kt][kk] = __builtin_bit_cast(bf16x8, z);
+      if constexpr (VREG) vB[kk] = __builtin_bit_cast(bf16x8, y);
     }
-    kB[kk] = __builtin_bit_cast(bf16x8, z);
-    if constexpr (VREG) vB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   wait_vmcnt<0>();                    // the loop's waits count only LDS loads
   asm volatile("" ::: "memory");
@@ -433,14 +454,16 @@ __global__ void __launch_bounds__(NWK * 64)
     dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
                 min(C::BK, klim), lds, wave * C::VBPW, C::VBPW, lane);
   float* const xch = reinterpret_cast<float*>(stage_base + NS * C::STAGE);   // DS > 1 only
-  const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
+  const int wk_valid = min(32 * KW, klim - wk0);      // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
-  f32x16 dKt[DBH], dVt[DBH];
+  f32x16 dKt[DBH][KW], dVt[DBH][KW];
 #pragma unroll
   for (int db = 0; db < DBH; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dKt[db][i] = dVt[db][i] = 0.f;
+    for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dKt[db][kt][i] = dVt[db][kt][i] = 0.f;
 
   // ---- the query stages of this item, NS-1 stages ahead in an LDS ring
   StageIter s0;
@@ -520,65 +543,84 @@ __global__ void __launch_bounds__(NWK * 64)
       // skip / full / masked for this wave's keys against the stage's queries
       int kind;
       if (wk_valid <= 0 || nrows <= 0 || sq_hi < wkp_lo || (pr.W > 0 && sq_lo - wkp_hi >= pr.W)) kind = 0;
-      else if (wk_valid == 32 && nrows == kStageRows && sq_lo >= wkp_hi &&
+      else if (wk_valid == 32 * KW && nrows == kStageRows && sq_lo >= wkp_hi &&
                (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
       else kind = 2;
-      f32x16 s, dp;
+      f32x16 s[KW], dp[KW];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kt][i] = dp[kt][i] = 0.f;
       if (kind != 0) {
 #pragma unroll
         for (int kk = 0; kk < KTH; ++kk) {
           const int kc = dh * KTH + kk;
-          const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + l32, kc, hf);
-          s = mfma32(row_operand<D>(Qs, l32, kc, hf), kB[kk], s);
-          dp = mfma32(row_operand<D>(DOs, l32, kc, hf), vb, dp);
+          const bf16x8 qa = row_operand<D>(Qs, l32, kc, hf);
+          const bf16x8 da = row_operand<D>(DOs, l32, kc, hf);
+#pragma unroll
+          for (int kt = 0; kt < KW; ++kt) {
+            const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + 32 * kt + l32, kc, hf);
+            s[kt] = mfma32(qa, kB[kt][kk], s[kt]);
+            dp[kt] = mfma32(da, vb, dp[kt]);
+          }
           if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (DS > 1) {
         // partial S and dP of the DS waves sharing these keys meet in LDS
         // (all of them share `kind`); summed in index order by every wave
-        float* mine = xch + (wave * 64 + lane) * 32;
+        // layout [wave][float4 j][lane] (S in j = 0..3, dP in 4..7): each
+        // 16-byte access of a wave covers 1 KiB contiguous
+        float4* const x4 = reinterpret_cast<float4*>(xch);
         if (kind != 0)
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            *reinterpret_cast<float4*>(mine + 4 * i4) =
-                make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
-            *reinterpret_cast<float4*>(mine + 16 + 4 * i4) =
-                make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
+            x4[(wave * 8 + i4) * 64 + lane] =
+                make_float4(s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]);
+            x4[(wave * 8 + 4 + i4) * 64 + lane] =
+                make_float4(dp[0][4 * i4], dp[0][4 * i4 + 1], dp[0][4 * i4 + 2], dp[0][4 * i4 + 3]);
           }
         block_sync();
         if (kind != 0)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float ts = 0.f, td = 0.f;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
 #pragma unroll
             for (int pp = 0; pp < DS; ++pp) {
-              const float* o = xch + ((wave - dh + pp) * 64 + lane) * 32;
-              const float vs = pp == dh ? s[i] : o[i];
-              const float vd = pp == dh ? dp[i] : o[16 + i];
-              ts = pp == 0 ? vs : ts + vs;
-              td = pp == 0 ? vd : td + vd;
+              const int w = wave - dh + pp;
+              const float4 vs = pp == dh ? make_float4(s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3])
+                                         : x4[(w * 8 + i4) * 64 + lane];
+              const float4 vd = pp == dh ? make_float4(dp[0][4 * i4], dp[0][4 * i4 + 1], dp[0][4 * i4 + 2], dp[0][4 * i4 + 3])
+                                         : x4[(w * 8 + 4 + i4) * 64 + lane];
+              if (pp == 0) {
+                ts4 = vs;
+                td4 = vd;
+              } else {
+                ts4.x += vs.x; ts4.y += vs.y; ts4.z += vs.z; ts4.w += vs.w;
+                td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
+              }
             }
-            s[i] = ts;
-            dp[i] = td;
+            s[0][4 * i4] = ts4.x; s[0][4 * i4 + 1] = ts4.y; s[0][4 * i4 + 2] = ts4.z; s[0][4 * i4 + 3] = ts4.w;
+            dp[0][4 * i4] = td4.x; dp[0][4 * i4 + 1] = td4.y; dp[0][4 * i4 + 2] = td4.z; dp[0][4 * i4 + 3] = td4.w;
           }
       }
       if (kind != 0) {
-        bf16x8 pB[2], dsB[2];
+        bf16x8 pB[KW][2], dsB[KW][2];
         if (kind == 2) {
           // query qc (+4*hf) of the stage is visible to this lane's key iff
           // 0 <= qpos - kpos < window and qc < nrows (branch-free); hidden
           // scores become -inf, so p = exp2(-inf - lse2) = 0 below.
-          int e0 = sq_lo + 4 * hf - kpos;
-          int n0 = (kvalid ? nrows : 0) - 4 * hf;
-          asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qc = 8 * (i >> 2) + (i & 3);           // query row - 4*hf
-            const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
-            s[i] = vis ? s[i] : -INFINITY;
+          for (int kt = 0; kt < KW; ++kt) {
+            int e0 = sq_lo + 4 * hf - kpos[kt];
+            int n0 = (kvalid[kt] ? nrows : 0) - 4 * hf;
+            asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int qc = 8 * (i >> 2) + (i & 3);           // query row - 4*hf
+              const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
+              s[kt][i] = vis ? s[kt][i] : -INFINITY;
+            }
           }
         }
 #pragma unroll
@@ -590,10 +632,13 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;                       // register index
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
-            const float ds = p * (dp[i] - dv4[e]);
-            pB[i >> 3][i & 7] = (__bf16)p;
-            dsB[i >> 3][i & 7] = (__bf16)ds;
+#pragma unroll
+            for (int kt = 0; kt < KW; ++kt) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -lv[e]));
+              const float ds = p * (dp[kt][i] - dv4[e]);
+              pB[kt][i >> 3][i & 7] = (__bf16)p;
+              dsB[kt][i >> 3][i & 7] = (__bf16)ds;
+            }
           }
         }
 #pragma unroll
@@ -601,8 +646,13 @@ __global__ void __launch_bounds__(NWK * 64)
           const int col = (dh * DBH + db) * 32;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            dVt[db] = mfma32(trans_operand<D>(DOs, 0, col, ks, lane), pB[ks], dVt[db]);
-            dKt[db] = mfma32(trans_operand<D>(Qs, 0, col, ks, lane), dsB[ks], dKt[db]);
+            const bf16x8 da = trans_operand<D>(DOs, 0, col, ks, lane);
+            const bf16x8 qa = trans_operand<D>(Qs, 0, col, ks, lane);
+#pragma unroll
+            for (int kt = 0; kt < KW; ++kt) {
+              dVt[db][kt] = mfma32(da, pB[kt][ks], dVt[db][kt]);
+              dKt[db][kt] = mfma32(qa, dsB[kt][ks], dKt[db][kt]);
+            }
           }
           if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
@@ -622,33 +672,38 @@ __global__ void __launch_bounds__(NWK * 64)
     ++idx;
   }
 
-  // ---- write dK (scaled) and dV for this lane's key
-  if (my_k < seg_len - it.k0 && it.k0 + my_k < seg_len) {
-    const bool partial = it.seg < 0 && sh.slots > 1;
+  // ---- write dK (scaled) and dV for this lane's keys
+  const bool partial = it.seg < 0 && sh.slots > 1;
 #pragma unroll
-    for (int db = 0; db < DBH; ++db)
+  for (int kt = 0; kt < KW; ++kt) {
+    if (my_k[kt] < seg_len - it.k0) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
-        if (partial) {
-          const int64_t o = (((int64_t)it.slot * pr.P + it.k0 + my_k) * pr.Hkv + c) * D + d;
-          *reinterpret_cast<float4*>(part_k + o) =
-              make_float4(dKt[db][4 * g4] * pr.scale, dKt[db][4 * g4 + 1] * pr.scale,
-                          dKt[db][4 * g4 + 2] * pr.scale, dKt[db][4 * g4 + 3] * pr.scale);
-          *reinterpret_cast<float4*>(part_v + o) =
-              make_float4(dVt[db][4 * g4], dVt[db][4 * g4 + 1], dVt[db][4 * g4 + 2], dVt[db][4 * g4 + 3]);
-        } else {
-          const int64_t o = krow * kstride + (int64_t)c * D + d;
-          union { __bf16 h[4]; uint2 u; } pk, pv;
+      for (int db = 0; db < DBH; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pk.h[e] = (__bf16)(dKt[db][4 * g4 + e] * pr.scale);
-            pv.h[e] = (__bf16)dVt[db][4 * g4 + e];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
+          const f32x16& ak = dKt[db][kt];
+          const f32x16& av = dVt[db][kt];
+          if (partial) {
+            const int64_t o = (((int64_t)it.slot * pr.P + it.k0 + my_k[kt]) * pr.Hkv + c) * D + d;
+            *reinterpret_cast<float4*>(part_k + o) =
+                make_float4(ak[4 * g4] * pr.scale, ak[4 * g4 + 1] * pr.scale, ak[4 * g4 + 2] * pr.scale,
+                            ak[4 * g4 + 3] * pr.scale);
+            *reinterpret_cast<float4*>(part_v + o) =
+                make_float4(av[4 * g4], av[4 * g4 + 1], av[4 * g4 + 2], av[4 * g4 + 3]);
+          } else {
+            const int64_t o = krow[kt] * kstride + (int64_t)c * D + d;
+            union { __bf16 h[4]; uint2 u; } pk, pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pk.h[e] = (__bf16)(ak[4 * g4 + e] * pr.scale);
+              pv.h[e] = (__bf16)av[4 * g4 + e];
+            }
+            *reinterpret_cast<uint2*>(dk + o) = pk.u;
+            *reinterpret_cast<uint2*>(dv + o) = pv.u;
           }
-          *reinterpret_cast<uint2*>(dk + o) = pk.u;
-          *reinterpret_cast<uint2*>(dv + o) = pv.u;
         }
-      }
+    }
   }
 }
 
@@ -720,10 +775,18 @@ __global__ void __launch_bounds__(256)
 
 // Waves per workgroup and head-dim split (DS waves share rows, each with
 // D/DS dims of state): dQ runs two waves per SIMD up to D = 256; dK/dV up to
-// D = 128; the rest one per SIMD.  D = 512 splits four ways.
+// D = 128; the rest one per SIMD.  dQ splits the head dim in two above
+// D = 128 (at D = 512 a wave then holds 256 dims of Q^T, dO^T and dQ in
+// VGPRs plus accumulation registers, and two 32-row slices share each K/V
+// tile); dK/dV splits D = 512 four ways.
 inline int dq_waves(int D) { return D <= 256 ? 8 : 4; }
 inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
-inline int dq_split(int D) { return D <= 128 ? 1 : (D <= 256 ? 2 : 4); }
+// Key tiles per wave of the dK/dV kernel.  Two tiles (one wave per SIMD)
+// halve the LDS reads per MFMA but lose the second wave's latency hiding;
+// measured slower at D = 128 (11.6 ms against 9.9 ms on the Qwen3-8B-shaped
+// layer), so every head dim runs one tile per wave.
+inline int kv_tiles_per_wave(int) { return 1; }
+inline int dq_split(int D) { return D <= 128 ? 1 : 2; }
 inline int kv_split(int D) { return D <= 128 ? 1 : (D <= 256 ? 2 : 4); }
 
 struct BwdPlan {
@@ -745,7 +808,7 @@ BwdPlan plan(const Problem& pr) {
   p.nbP = (pr.P + p.BM - 1) / p.BM;
   p.nbR = (pr.R + p.BM - 1) / p.BM;
   p.nwg_dq = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
-  const int BK = 32 * kv_waves(pr.D) / kv_split(pr.D);
+  const int BK = 32 * kv_tiles_per_wave(pr.D) * kv_waves(pr.D) / kv_split(pr.D);
   p.sh.nPt = (pr.P + BK - 1) / BK;
   p.sh.nRt = (pr.R + BK - 1) / BK;
   // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
@@ -770,15 +833,15 @@ BwdPlan plan(const Problem& pr) {
   return p;
 }
 
-template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG>
+template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG, int KW>
 hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                char* ws, hipStream_t stream) {
   using CQ = DqCfg<D, kDqBN, NW, DQNS, DS>;
-  using CK = KvCfg<D, NWK, KVNS, KDS, VREG>;
+  using CK = KvCfg<D, NWK, KVNS, KDS, VREG, KW>;
   static_assert(CQ::LDS_BYTES <= 160 * 1024 && CK::LDS_BYTES <= 160 * 1024, "LDS budget");
   static const hipError_t a1 = allow_lds(bwd_dq_kernel<D, kDqBN, NW, DQNS, DS>, CQ::LDS_BYTES);
-  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, CK::LDS_BYTES);
+  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   float* delta = reinterpret_cast<float*>(ws + p.off_delta);
@@ -804,7 +867,7 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
+    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
                stream, pr, p.sh, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
@@ -836,11 +899,11 @@ hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, cons
   const BwdPlan p = plan(pr);
   char* ws = static_cast<char*>(workspace);
   switch (pr.D) {
-    //                D  NW NWK BN DQNS KVNS DS KDS VREG
-    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 1, 4, 4, true>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    //                D  NW NWK BN DQNS KVNS DS KDS VREG KW
+    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 1, 2, 4, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

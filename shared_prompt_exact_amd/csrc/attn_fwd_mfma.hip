@@ -173,14 +173,15 @@ __global__ void __launch_bounds__(NW * 64)
       if constexpr (DS > 1) {
         // partial scores of the two halves meet in LDS (all waves pass the
         // barrier; both members of a pair have the same `kind`)
-        float* mine = xch + (wave * 64 + lane) * 16 * NB32;
-        const float* other = xch + ((wave ^ 1) * 64 + lane) * 16 * NB32;
+        // layout [wave][float4 j][lane]: each 16-byte store or load of a wave
+        // covers 1 KiB contiguous (no bank conflicts)
+        float4* const x4 = reinterpret_cast<float4*>(xch);
         if (kind != 0)
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4)
-              *reinterpret_cast<float4*>(mine + 16 * kb + 4 * i4) =
+              x4[(wave * 4 * NB32 + 4 * kb + i4) * 64 + lane] =
                   make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
         block_sync();
         if (kind != 0)
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(NW * 64)
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const float4 t = *reinterpret_cast<const float4*>(other + 16 * kb + 4 * i4);
+              const float4 t = x4[((wave ^ 1) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
               // lower half first in both waves: identical sums
               s[kb][4 * i4 + 0] = dh == 0 ? s[kb][4 * i4 + 0] + t.x : t.x + s[kb][4 * i4 + 0];
               s[kb][4 * i4 + 1] = dh == 0 ? s[kb][4 * i4 + 1] + t.y : t.y + s[kb][4 * i4 + 1];
