@@ -76,7 +76,8 @@ __global__ void __launch_bounds__(NW * 64)
   const int dh = wave % DS, wq = wave / DS;
   const int BM = 32 * NWQ / HG;
   const int NB = nbP + pr.N * nbR;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = balanced_block(blockIdx.x, pr.Hq / HG, NB);
+  if (L < 0) return;                          // grid padding (whole workgroup)
   const int hgi = L / NB, blk = L % NB;
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
@@ -388,9 +389,10 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- decode the work item (longest first, one KV head per XCD slice)
+  // ---- decode the work item (longest first within a KV head)
   const int per_head = sh.nPt * sh.slots + pr.N * sh.nRt;
-  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int Lid = balanced_block(blockIdx.x, pr.Hkv, per_head);
+  if (Lid < 0) return;                        // grid padding (whole workgroup)
   KvItem it;
   it.c = Lid / per_head;
   int x = Lid % per_head;
@@ -807,7 +809,7 @@ BwdPlan plan(const Problem& pr) {
   p.BM = 32 * (p.NW / p.DS) / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
   p.nbR = (pr.R + p.BM - 1) / p.BM;
-  p.nwg_dq = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
+  p.nwg_dq = balanced_grid(pr.Hq / p.HG, p.nbP + (int64_t)pr.N * p.nbR);
   const int BK = 32 * kv_tiles_per_wave(pr.D) * kv_waves(pr.D) / kv_split(pr.D);
   p.sh.nPt = (pr.P + BK - 1) / BK;
   p.sh.nRt = (pr.R + BK - 1) / BK;
@@ -823,7 +825,7 @@ BwdPlan plan(const Problem& pr) {
   p.sh.per_slot = rslots > 0 ? (pr.N + rslots - 1) / rslots : 1;
   if (rslots > 0) rslots = (pr.N + p.sh.per_slot - 1) / p.sh.per_slot;
   p.sh.slots = 1 + rslots;
-  p.nwg_kv = ((int64_t)p.sh.nPt * p.sh.slots + (int64_t)pr.N * p.sh.nRt) * pr.Hkv;
+  p.nwg_kv = balanced_grid(pr.Hkv, (int64_t)p.sh.nPt * p.sh.slots + (int64_t)pr.N * p.sh.nRt);
   p.off_delta = 0;
   p.off_lse2 = align256((size_t)pr.Hq * pr.T * sizeof(float));
   p.off_pk = 2 * p.off_lse2;

@@ -27,8 +27,8 @@
 //    LDS address is a per-lane base plus an immediate;
 //  * the O rescale runs only when a row's running max grows by more than
 //    2^8 (the softmax is exact for any reference max);
-//  * workgroups are ordered longest key range first and remapped so each
-//    XCD runs a contiguous slice of that order (one KV head's K/V per L2).
+//  * workgroups are ordered longest key range first and mapped so each XCD
+//    works on one head group at a time with an equal share of the work.
 #include "lds_tiles.h"
 
 namespace dualkv {
@@ -80,7 +80,8 @@ __global__ void __launch_bounds__(NW * 64)
   const int dh = wave % DS, wq = wave / DS;     // head-dim half, query slot
   const int BM = 32 * NWQ / HG;
   const int NB = nbP + pr.N * nbR;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = balanced_block(blockIdx.x, pr.Hq / HG, NB);
+  if (L < 0) return;                            // grid padding (whole workgroup)
   const int hgi = L / NB, blk = L % NB;
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
@@ -309,7 +310,7 @@ FwdPlan plan(const Problem& pr) {
   p.BM = 32 * (p.NW / p.DS) / p.HG;
   p.nbP = (pr.P + p.BM - 1) / p.BM;
   p.nbR = (pr.R + p.BM - 1) / p.BM;
-  p.nwg = (int64_t)(p.nbP + (int64_t)pr.N * p.nbR) * (pr.Hq / p.HG);
+  p.nwg = balanced_grid(pr.Hq / p.HG, p.nbP + (int64_t)pr.N * p.nbR);
   return p;
 }
 

@@ -42,15 +42,40 @@ __device__ __forceinline__ int perm16(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
-// Logical workgroup order: consecutive workgroup ids are dispatched round
-// robin over the 8 XCDs (each with its own L2).  Remap so that every XCD
-// works through one contiguous range of the logical order, which keeps the
-// K/V of one KV head inside one L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+// Workgroup -> logical block.  A launch's work is `units` groups of
+// `per_unit` logical blocks (a head group with its query blocks, or a KV
+// head with its key items), each group in longest-first order.  Workgroups
+// are dispatched round robin over the 8 XCDs (workgroup b runs on XCD b % 8
+// as that XCD's (b / 8)-th), and each XCD has its own L2.  So that every XCD
+// works on one unit's data at a time AND gets the same share of the work:
+//  * units a multiple of 8: XCD x takes whole units x, x + 8, ...;
+//  * 8 a multiple of units: S = 8 / units XCDs share a unit, XCD x taking
+//    every S-th block of it (offset x % S); the grid is padded to whole
+//    rounds and padding workgroups get -1;
+//  * otherwise the natural order.
+__device__ __forceinline__ int balanced_block(int bid, int units, int per_unit) {
   constexpr int X = 8;
-  const int q = nwg / X, r = nwg % X;
   const int xcd = bid % X, slot = bid / X;
-  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+  if (units % X == 0) {
+    const int k = slot / per_unit, item = slot - k * per_unit;
+    return (xcd + X * k) * per_unit + item;
+  }
+  if (X % units == 0) {
+    const int S = X / units;
+    const int item = slot * S + xcd % S;
+    return item < per_unit ? (xcd / S) * per_unit + item : -1;
+  }
+  return bid;
+}
+
+// Grid size for balanced_block.
+inline int64_t balanced_grid(int units, int64_t per_unit) {
+  constexpr int X = 8;
+  if (units % X != 0 && X % units == 0) {
+    const int S = X / units;
+    return X * ((per_unit + S - 1) / S);
+  }
+  return (int64_t)units * per_unit;
 }
 
 // Query heads handled together by one workgroup: the largest power of two
