@@ -291,7 +291,11 @@ struct KvCfg {
   static constexpr int DO_ELEMS = kStageRows * D;   // dO stage rows
   static constexpr int STAT = 2 * kStageRows * 2;   // LSE and delta, fp32 (in u16 units)
   static constexpr int STAGE = Q_ELEMS + DO_ELEMS + STAT;
-  static constexpr int XCH_BYTES = DS > 1 ? NWK * 64 * 32 * 4 : 0;   // partial S, dP
+  // partial S and dP of the head-dim split: both at once, or (when LDS is
+  // short) S then dP through the same half-size buffer
+  static constexpr int XCH_FULL = DS > 1 ? NWK * 64 * 32 * 4 : 0;
+  static constexpr bool XCH_TWO_PHASE = (V_ELEMS + NS * STAGE) * 2 + XCH_FULL > 160 * 1024;
+  static constexpr int XCH_BYTES = XCH_TWO_PHASE ? XCH_FULL / 2 : XCH_FULL;
   static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2 + XCH_BYTES;
   static constexpr int VBPW = V_ELEMS * 2 / 1024 / NWK;     // V blocks per wave
   static constexpr int QBLK = Q_ELEMS * 2 / 1024;           // blocks per Q (or dO) stage tile
@@ -571,40 +575,52 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       if constexpr (DS > 1) {
         // partial S and dP of the DS waves sharing these keys meet in LDS
         // (all of them share `kind`); summed in index order by every wave
-        // layout [wave][float4 j][lane] (S in j = 0..3, dP in 4..7): each
-        // 16-byte access of a wave covers 1 KiB contiguous
+        // layout [wave][float4 j][lane]: each 16-byte access of a wave covers
+        // 1 KiB contiguous.  One phase: S in j = 0..3, dP in 4..7; two
+        // phases: S, then dP, in j = 0..3 of a buffer half the size.
         float4* const x4 = reinterpret_cast<float4*>(xch);
-        if (kind != 0)
+        constexpr int J = C::XCH_TWO_PHASE ? 4 : 8;
+        auto put = [&](const f32x16& a, int j0) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            x4[(wave * J + j0 + i4) * 64 + lane] = make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
+        };
+        auto sum = [&](f32x16& a, int j0) {   // partials added in head-dim order
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            x4[(wave * 8 + i4) * 64 + lane] =
-                make_float4(s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3]);
-            x4[(wave * 8 + 4 + i4) * 64 + lane] =
-                make_float4(dp[0][4 * i4], dp[0][4 * i4 + 1], dp[0][4 * i4 + 2], dp[0][4 * i4 + 3]);
-          }
-        block_sync();
-        if (kind != 0)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
+            float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int pp = 0; pp < DS; ++pp) {
-              const int w = wave - dh + pp;
-              const float4 vs = pp == dh ? make_float4(s[0][4 * i4], s[0][4 * i4 + 1], s[0][4 * i4 + 2], s[0][4 * i4 + 3])
-                                         : x4[(w * 8 + i4) * 64 + lane];
-              const float4 vd = pp == dh ? make_float4(dp[0][4 * i4], dp[0][4 * i4 + 1], dp[0][4 * i4 + 2], dp[0][4 * i4 + 3])
-                                         : x4[(w * 8 + 4 + i4) * 64 + lane];
+              const float4 v4 = pp == dh ? make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3])
+                                         : x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
               if (pp == 0) {
-                ts4 = vs;
-                td4 = vd;
+                t4 = v4;
               } else {
-                ts4.x += vs.x; ts4.y += vs.y; ts4.z += vs.z; ts4.w += vs.w;
-                td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
+                t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
               }
             }
-            s[0][4 * i4] = ts4.x; s[0][4 * i4 + 1] = ts4.y; s[0][4 * i4 + 2] = ts4.z; s[0][4 * i4 + 3] = ts4.w;
-            dp[0][4 * i4] = td4.x; dp[0][4 * i4 + 1] = td4.y; dp[0][4 * i4 + 2] = td4.z; dp[0][4 * i4 + 3] = td4.w;
+            a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
           }
+        };
+        if constexpr (C::XCH_TWO_PHASE) {
+          if (kind != 0) put(s[0], 0);
+          block_sync();
+          if (kind != 0) sum(s[0], 0);
+          block_sync();                       // every wave has read the S partials
+          if (kind != 0) put(dp[0], 0);
+          block_sync();
+          if (kind != 0) sum(dp[0], 0);
+        } else {
+          if (kind != 0) {
+            put(s[0], 0);
+            put(dp[0], 4);
+          }
+          block_sync();
+          if (kind != 0) {
+            sum(s[0], 0);
+            sum(dp[0], 4);
+          }
+        }
       }
       if (kind != 0) {
         bf16x8 pB[KW][2], dsB[KW][2];
@@ -776,20 +792,20 @@ __global__ void __launch_bounds__(256)
 // ------------------------------------------------------------------ planning
 
 // Waves per workgroup and head-dim split (DS waves share rows, each with
-// D/DS dims of state): dQ runs two waves per SIMD up to D = 256; dK/dV up to
-// D = 128; the rest one per SIMD.  dQ splits the head dim in two above
-// D = 128 (at D = 512 a wave then holds 256 dims of Q^T, dO^T and dQ in
-// VGPRs plus accumulation registers, and two 32-row slices share each K/V
-// tile); dK/dV splits D = 512 four ways.
-inline int dq_waves(int D) { return D <= 256 ? 8 : 4; }
+// D/DS dims of state): two waves per SIMD up to D = 128, one above.  Both
+// kernels split the head dim in two only at D = 512: a wave then holds at
+// most 256 dims of its operands and accumulators (VGPRs plus accumulation
+// registers), and the waves of a workgroup cover several 32-row (or
+// 32-key) slices that share each streamed tile.
+inline int dq_waves(int D) { return D <= 128 ? 8 : 4; }
 inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
 // Key tiles per wave of the dK/dV kernel.  Two tiles (one wave per SIMD)
 // halve the LDS reads per MFMA but lose the second wave's latency hiding;
 // measured slower at D = 128 (11.6 ms against 9.9 ms on the Qwen3-8B-shaped
 // layer), so every head dim runs one tile per wave.
 inline int kv_tiles_per_wave(int) { return 1; }
-inline int dq_split(int D) { return D <= 128 ? 1 : 2; }
-inline int kv_split(int D) { return D <= 128 ? 1 : (D <= 256 ? 2 : 4); }
+inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
+inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
 struct BwdPlan {
   int NW, DS, HG, BM, nbP, nbR;
@@ -904,8 +920,8 @@ hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, cons
     //                D  NW NWK BN DQNS KVNS DS KDS VREG KW
     case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 256: return run<256, 8, 4, 32, 3, 2, 2, 2, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 1, 2, 4, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
