@@ -324,6 +324,7 @@ struct KvShape {
   int slots;          // slots per prompt tile
   int per_slot;       // responses per slot (slots >= 2)
   int nPt, nRt;       // prompt / response key tiles per KV head
+  int t0;             // first prompt tile a response query can see (window)
 };
 
 // Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
@@ -394,23 +395,26 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- decode the work item (longest first within a KV head)
-  const int per_head = sh.nPt * sh.slots + pr.N * sh.nRt;
+  const int per_head = (sh.nPt - sh.t0) * (sh.slots - 1) + sh.nPt + pr.N * sh.nRt;
   const int Lid = balanced_block(blockIdx.x, pr.Hkv, per_head);
   if (Lid < 0) return;                        // grid padding (whole workgroup)
   KvItem it;
   it.c = Lid / per_head;
   int x = Lid % per_head;
-  if (x < sh.nPt * sh.slots) {
+  // response slots exist only for prompt tiles t0 .. nPt-1 (all of them
+  // without a window)
+  const int nPtR = sh.nPt - sh.t0;
+  if (x < nPtR * (sh.slots - 1) + sh.nPt) {
     it.seg = -1;
-    if (sh.slots > 1 && x < sh.nPt * (sh.slots - 1)) {   // response slots first
-      it.slot = 1 + x / sh.nPt;
-      it.k0 = (x % sh.nPt) * C::BK;
+    if (x < nPtR * (sh.slots - 1)) {                      // response slots first
+      it.slot = 1 + x / nPtR;
+      it.k0 = (sh.t0 + x % nPtR) * C::BK;
     } else {                                              // then the prompt slot
       it.slot = 0;
-      it.k0 = (x - sh.nPt * (sh.slots - 1)) * C::BK;
+      it.k0 = (x - nPtR * (sh.slots - 1)) * C::BK;
     }
   } else {
-    x -= sh.nPt * sh.slots;
+    x -= nPtR * (sh.slots - 1) + sh.nPt;
     it.seg = x % pr.N;
     it.k0 = (x / pr.N) * C::BK;
     it.slot = 0;
@@ -691,7 +695,8 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   }
 
   // ---- write dK (scaled) and dV for this lane's keys
-  const bool partial = it.seg < 0 && sh.slots > 1;
+  // prompt tiles with response slots write fp32 partials for the reduction
+  const bool partial = it.seg < 0 && sh.slots > 1 && it.k0 >= sh.t0 * C::BK;
 #pragma unroll
   for (int kt = 0; kt < KW; ++kt) {
     if (my_k[kt] < seg_len - it.k0) {
@@ -768,16 +773,20 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------ slot reduction
 
+// Prompt rows whose key tiles wrote per-slot fp32 partials: float4 index
+// i0 .. i0+n4-1 of the [P, Hkv, D] prompt block (slot stride `stride4`).
 __global__ void __launch_bounds__(256)
     reduce_slots_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v,
-                        int slots, int64_t n4, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x) {
+                        int slots, int64_t stride4, int64_t i0, int64_t n4, uint16_t* __restrict__ dk,
+                        uint16_t* __restrict__ dv) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n4;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = i0 + j;
     float4 a = reinterpret_cast<const float4*>(part_k)[i];
     float4 b = reinterpret_cast<const float4*>(part_v)[i];
     for (int s = 1; s < slots; ++s) {     // ascending slot order
-      const float4 x = reinterpret_cast<const float4*>(part_k)[s * n4 + i];
-      const float4 y = reinterpret_cast<const float4*>(part_v)[s * n4 + i];
+      const float4 x = reinterpret_cast<const float4*>(part_k)[s * stride4 + i];
+      const float4 y = reinterpret_cast<const float4*>(part_v)[s * stride4 + i];
       a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
       b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
     }
@@ -811,6 +820,7 @@ struct BwdPlan {
   int NW, DS, HG, BM, nbP, nbR;
   int64_t nwg_dq;
   KvShape sh;
+  int BK;
   int64_t nwg_kv;
   size_t off_delta, off_lse2, off_pk, off_pv, bytes;
 };
@@ -841,7 +851,13 @@ BwdPlan plan(const Problem& pr) {
   p.sh.per_slot = rslots > 0 ? (pr.N + rslots - 1) / rslots : 1;
   if (rslots > 0) rslots = (pr.N + p.sh.per_slot - 1) / p.sh.per_slot;
   p.sh.slots = 1 + rslots;
-  p.nwg_kv = balanced_grid(pr.Hkv, (int64_t)p.sh.nPt * p.sh.slots + (int64_t)pr.N * p.sh.nRt);
+  // With a window, response query r (position P + r) sees prompt keys from
+  // P + r - W + 1 on, so prompt keys below P - W + 1 get no response term.
+  const int first_seen = pr.W > 0 ? max(0, pr.P - pr.W + 1) : 0;
+  p.sh.t0 = rslots > 0 ? min(p.sh.nPt, first_seen / BK) : p.sh.nPt;
+  p.nwg_kv = balanced_grid(pr.Hkv, (int64_t)(p.sh.nPt - p.sh.t0) * (p.sh.slots - 1) + p.sh.nPt +
+                                       (int64_t)pr.N * p.sh.nRt);
+  p.BK = BK;
   p.off_delta = 0;
   p.off_lse2 = align256((size_t)pr.Hq * pr.T * sizeof(float));
   p.off_pk = 2 * p.off_lse2;
@@ -890,12 +906,16 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
   }
-  if (p.sh.slots > 1 && pr.P > 0) {
-    const int64_t n4 = (int64_t)pr.P * pr.Hkv * D / 4;
+  if (p.sh.slots > 1 && p.sh.t0 < p.sh.nPt) {
+    // prompt rows t0*BK .. P-1: the rows whose tiles wrote slot partials
+    const int64_t r0 = (int64_t)p.sh.t0 * p.BK;
+    const int64_t row4 = (int64_t)pr.Hkv * D / 4;        // float4s per prompt row
+    const int64_t n4 = (pr.P - r0) * row4;
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     e = launch("bwd_reduce", reduce_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pk, pv,
-               p.sh.slots, n4, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+               p.sh.slots, (int64_t)pr.P * row4, r0 * row4, n4, static_cast<uint16_t*>(dk),
+               static_cast<uint16_t*>(dv));
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -73,6 +73,10 @@ MID = [
     W("mid_d256_valid", "bf16", 3, 100, 64, 8, 2, 256, 0, seed=32, value_scale=1.0, len_range=(1, 64)),
     # the benchmark value scale (0.5) at a reduced size
     W("mid_half", "bf16", 4, 256, 128, 8, 2, 128, 0, seed=29, value_scale=0.5),
+    # windows far shorter than the prompt: leading prompt key tiles get no
+    # response term (no slot partials there), head dims 128 and 256
+    W("mid_window_long", "bf16", 2, 700, 120, 4, 2, 128, 100, seed=33, value_scale=1.0),
+    W("mid_window_d256", "bf16", 3, 400, 90, 4, 1, 256, 64, seed=34, value_scale=1.0),
 ]
 
 
