@@ -50,7 +50,7 @@ struct DqCfg {
   static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
   static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 32 * (BN / 32) * 4 : 0;   // partial S, dP
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 32 * 4 : 0;   // partial S, dP of a 32-key sub-tile
   static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
   static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
   static constexpr int BPW = KBLK / NW;
@@ -153,55 +153,47 @@ __global__ void __launch_bounds__(NW * 64)
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
       const uint16_t* Ks = lds + SLOT * C::STAGE;
       const uint16_t* Vs = Ks + C::K_ELEMS;
-      f32x16 s[NB32], dp[NB32];
+      // 32-key sub-tiles one after the other: a BN-key tile costs one
+      // barrier, the registers of one 32-key sub-tile
 #pragma unroll
-      for (int kb = 0; kb < NB32; ++kb)
+      for (int kb = 0; kb < NB32; ++kb) {
+        f32x16 s, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
-      if (kind != 0) {
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        if (kind != 0) {
 #pragma unroll
-        for (int kk = 0; kk < KTH; ++kk) {
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb) {
-            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
-            dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp[kb]);
+          for (int kk = 0; kk < KTH; ++kk) {
+            s = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s);
+            dp = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp);
+            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
           }
-          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if constexpr (DS > 1) {
-        // partial S and dP of the DS waves sharing these rows meet in LDS;
-        // every wave adds the DS partials in index order (its own from
-        // registers), so all of them hold bit-identical sums
-        // layout [wave][float4 j][lane] (S in j = 8kb .. 8kb+3, dP in
-        // 8kb+4 .. 8kb+7): each 16-byte access of a wave covers 1 KiB
-        // contiguous (no bank conflicts)
-        float4* const x4 = reinterpret_cast<float4*>(xch);
-        constexpr int J = 8 * NB32;
-        if (kind != 0)
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
+        if constexpr (DS > 1) {
+          // partial S and dP of the DS waves sharing these rows meet in LDS;
+          // every wave adds the DS partials in index order (its own from
+          // registers), so all of them hold bit-identical sums.  Layout
+          // [wave][float4 j][lane] (S in j = 0..3, dP in 4..7): each 16-byte
+          // access of a wave covers 1 KiB contiguous (no bank conflicts).
+          float4* const x4 = reinterpret_cast<float4*>(xch);
+          if (kind != 0)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              x4[(wave * J + 8 * kb + i4) * 64 + lane] =
-                  make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
-              x4[(wave * J + 8 * kb + 4 + i4) * 64 + lane] =
-                  make_float4(dp[kb][4 * i4], dp[kb][4 * i4 + 1], dp[kb][4 * i4 + 2], dp[kb][4 * i4 + 3]);
+              x4[(wave * 8 + i4) * 64 + lane] = make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+              x4[(wave * 8 + 4 + i4) * 64 + lane] =
+                  make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
             }
-        block_sync();
-        if (kind != 0)
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
+          block_sync();
+          if (kind != 0)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
 #pragma unroll
               for (int pp = 0; pp < DS; ++pp) {
                 const int w = wave - dh + pp;
-                const float4 vs = pp == dh ? make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3])
-                                           : x4[(w * J + 8 * kb + i4) * 64 + lane];
-                const float4 vd = pp == dh ? make_float4(dp[kb][4 * i4], dp[kb][4 * i4 + 1], dp[kb][4 * i4 + 2], dp[kb][4 * i4 + 3])
-                                           : x4[(w * J + 8 * kb + 4 + i4) * 64 + lane];
+                const float4 vs = pp == dh ? make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3])
+                                           : x4[(w * 8 + i4) * 64 + lane];
+                const float4 vd = pp == dh ? make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3])
+                                           : x4[(w * 8 + 4 + i4) * 64 + lane];
                 if (pp == 0) {
                   ts4 = vs;
                   td4 = vd;
@@ -210,42 +202,40 @@ __global__ void __launch_bounds__(NW * 64)
                   td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
                 }
               }
-              s[kb][4 * i4] = ts4.x; s[kb][4 * i4 + 1] = ts4.y; s[kb][4 * i4 + 2] = ts4.z; s[kb][4 * i4 + 3] = ts4.w;
-              dp[kb][4 * i4] = td4.x; dp[kb][4 * i4 + 1] = td4.y; dp[kb][4 * i4 + 2] = td4.z; dp[kb][4 * i4 + 3] = td4.w;
+              s[4 * i4] = ts4.x; s[4 * i4 + 1] = ts4.y; s[4 * i4 + 2] = ts4.z; s[4 * i4 + 3] = ts4.w;
+              dp[4 * i4] = td4.x; dp[4 * i4 + 1] = td4.y; dp[4 * i4 + 2] = td4.z; dp[4 * i4 + 3] = td4.w;
             }
-      }
-      if (kind != 0) {
-        bf16x8 dsB[K16];
-        if (kind == 2) {
-          // hidden scores become -inf: p = exp2(-inf - lse2) = 0 below
-          int d0 = qpos - kt.pos0 - 4 * hf;
-          int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
-          asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
+          if (kb + 1 < NB32) block_sync();     // partials read before the next sub-tile's
+        }
+        if (kind != 0) {
+          if (kind == 2) {
+            // hidden scores become -inf: p = exp2(-inf - lse2) = 0 below
+            int d0 = qpos - kt.pos0 - 4 * hf - kb * 32;
+            int lim0 = (qvalid ? kt.lim : 0) - 4 * hf - kb * 32;
+            asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              const int kc = 8 * (i >> 2) + (i & 3);
               const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
-              s[kb][i] = vis ? s[kb][i] : -INFINITY;
+              s[i] = vis ? s[i] : -INFINITY;
             }
-        }
-#pragma unroll
-        for (int kb = 0; kb < NB32; ++kb)
+          }
+          bf16x8 dsB[2];
 #pragma unroll
           for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int i = 8 * hs + j;
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
-              dsB[2 * kb + hs][j] = (__bf16)(p * (dp[kb][i] - dlt));
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
+              dsB[hs][j] = (__bf16)(p * (dp[i] - dlt));
             }
 #pragma unroll
-        for (int db = 0; db < DBH; ++db) {
+          for (int db = 0; db < DBH; ++db) {
 #pragma unroll
-          for (int ks = 0; ks < K16; ++ks)
-            acc[db] = mfma32(trans_operand<D>(Ks, 0, (dh * DBH + db) * 32, ks, lane), dsB[ks], acc[db]);
-          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            for (int hs = 0; hs < 2; ++hs)
+              acc[db] = mfma32(trans_operand<D>(Ks, 0, (dh * DBH + db) * 32, 2 * kb + hs, lane), dsB[hs], acc[db]);
+            if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     };
