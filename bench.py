@@ -10,6 +10,10 @@ Inputs are resident in HBM before the timed region.  `value` is useful
 fwd+bwd TFLOP/s: visible (query, key) pairs of the packed layout times
 14*D*Hq, divided by the measured step time.
 
+A workload is one layer shape (one prompt group, the single-group entry
+points) or a grouped micro-batch (several prompt groups laid one after the
+other, the *_groups entry points); the step is the same.
+
 Also reported: forward / backward alone, the same library on the replicated
 N(P+R) layout (P'=0, R'=P+R, valid lengths P+L_n: N independent causal
 sequences) and the speedup over it, the dominant kernel's roofline (HIP
@@ -37,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--workload", default="qwen3_8b",
+                    help="a layer shape (one prompt group) or a grouped micro-batch")
     ap.add_argument("--no-replicated", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -56,10 +61,11 @@ def timed(fn, steps, torch):
     return s.elapsed_time(e) / steps
 
 
-def cpu_baseline(w, x, seconds):
-    """The fp64 oracle on a bounded sample: replicated sequences n = 0, 1, ...
-    of KV head 0 (all its query heads), forward + backward, until `seconds`
-    have passed.  Rate in useful TFLOP/s of the pairs computed."""
+def cpu_baseline(w, groups, x, seconds):
+    """The fp64 oracle on a bounded sample: the replicated sequences of the
+    groups in order (group 0's n = 0, 1, ..., then group 1's ...), KV head 0
+    (all its query heads), forward + backward, until `seconds` have passed.
+    Rate in useful TFLOP/s of the pairs computed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -67,26 +73,29 @@ def cpu_baseline(w, x, seconds):
     from shared_prompt_exact_amd import workcount
 
     g = w.n_q_heads // w.n_kv_heads
-    L = [w.resp_len] * w.n_resp if x.valid_len is None else [int(a) for a in x.valid_len]
-    done, t0, flops = 0, time.perf_counter(), 0
-    while done < w.n_resp:
-        n = done
-        idx = replicated.sequence_rows(n, w.n_resp, w.prompt_len, w.resp_len)
-        seq_valid = w.prompt_len + L[n]
-        replicated.causal_sequence(x.q[idx].astype(np.float64), x.k[idx].astype(np.float64),
-                                   x.v[idx].astype(np.float64), x.do[idx].astype(np.float64),
-                                   seq_valid, w.window, None, 1024, kv_heads=[0])
-        pairs = workcount.replicated_pairs(1, w.prompt_len, L[n], w.window)
-        flops += 14 * pairs * g * w.head_dim
-        done += 1
+    total = sum(N for N, _, _ in groups)
+    done, t0, flops, row0, vl0 = 0, time.perf_counter(), 0, 0, 0
+    for N, P, R in groups:
+        L = [R] * N if x.valid_len is None else [int(a) for a in x.valid_len[vl0:vl0 + N]]
+        for n in range(N):
+            idx = row0 + replicated.sequence_rows(n, N, P, R)
+            replicated.causal_sequence(x.q[idx].astype(np.float64), x.k[idx].astype(np.float64),
+                                       x.v[idx].astype(np.float64), x.do[idx].astype(np.float64),
+                                       P + L[n], w.window, None, 1024, kv_heads=[0])
+            flops += 14 * workcount.replicated_pairs(1, P, L[n], w.window) * g * w.head_dim
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
         if time.perf_counter() - t0 >= seconds:
             break
+        row0 += P + N * R
+        vl0 += N
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"fp64 oracle (replicated causal attention + analytic backward), KV head 0 "
-                       f"of {w.n_kv_heads} with its {g} query heads, {done} of {w.n_resp} sequences "
-                       f"of {w.prompt_len}+R tokens, {dt:.1f} s; rate counts useful pairs of the sample")}
+                       f"of {w.n_kv_heads} with its {g} query heads, {done} of {total} sequences "
+                       f"(prompt + response), {dt:.1f} s; rate counts useful pairs of the sample")}
 
 
 def main():
@@ -106,45 +115,81 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = workloads.WORKLOADS[args.workload]
-    N, P, R, D, Hq, Hkv, Wn = (w.n_resp, w.prompt_len, w.resp_len, w.head_dim, w.n_q_heads,
-                               w.n_kv_heads, w.window)
+    grouped = args.workload in workloads.GROUPED
+    if grouped:
+        w = workloads.GROUPED[args.workload]
+        groups = w.groups
+    else:
+        w = workloads.WORKLOADS[args.workload]
+        groups = ((w.n_resp, w.prompt_len, w.resp_len),)
+    D, Hq, Hkv, Wn = w.head_dim, w.n_q_heads, w.n_kv_heads, w.window
+    T, T_rep = w.packed_len, w.replicated_len
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
-    x = workloads.generate(w)
+    x = workloads.generate_groups(w) if grouped else workloads.generate(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     to = lambda a: torch.from_numpy(a).to(tdt).to(dev)
     q, k, v, do = to(x.q), to(x.k), to(x.v), to(x.do)
     valid = None if x.valid_len is None else torch.from_numpy(x.valid_len).to(dev)
-    L = [R] * N if x.valid_len is None else x.valid_len.tolist()
+    Ls, vl0 = [], 0          # valid lengths per group
+    for N, P, R in groups:
+        Ls.append([R] * N if x.valid_len is None else x.valid_len[vl0:vl0 + N].tolist())
+        vl0 += N
 
-    pairs = workcount.visible_pairs(N, P, R, Wn, L)
-    rep_pairs = workcount.replicated_pairs(N, P, R, Wn, L)
+    pairs = sum(workcount.visible_pairs(N, P, R, Wn, L) for (N, P, R), L in zip(groups, Ls))
+    rep_pairs = sum(workcount.replicated_pairs(N, P, R, Wn, L) for (N, P, R), L in zip(groups, Ls))
     fl = workcount.flops(pairs, Hq, D)
+
+    # The library calls of one step, on one group (the single-group entry
+    # points) or on several (the grouped ones).
+    if grouped:
+        def repack(src, direction, out):
+            return dk.dualkv_repack_groups(src, groups, direction, out=out)
+
+        def lib_fwd(q_, k_, v_, gs, **kw_):
+            return dk.dualkv_fwd_groups(q_, k_, v_, gs, **kw_)
+
+        def lib_bwd(q_, k_, v_, o_, l_, do_, gs, **kw_):
+            return dk.dualkv_bwd_groups(q_, k_, v_, o_, l_, do_, gs, **kw_)
+
+        def lib_ws(q_, k_, gs, **kw_):
+            return dk.dualkv_bwd_groups_workspace_bytes(q_, k_, gs, **kw_)
+    else:
+        def repack(src, direction, out):
+            return dk.dualkv_repack(src, *groups[0], direction, out=out)
+
+        def lib_fwd(q_, k_, v_, gs, **kw_):
+            return dk.dualkv_fwd(q_, k_, v_, *gs[0], **kw_)
+
+        def lib_bwd(q_, k_, v_, o_, l_, do_, gs, **kw_):
+            return dk.dualkv_bwd(q_, k_, v_, o_, l_, do_, *gs[0], **kw_)
+
+        def lib_ws(q_, k_, gs, **kw_):
+            return dk.dualkv_bwd_workspace_bytes(q_, k_, *gs[0], **kw_)
 
     # per-micro-batch token rows (id, position, loss mask, advantage bits)
     g = torch.Generator().manual_seed(w.seed)
-    tok_rep = torch.randint(0, 2 ** 31 - 1, (N * (P + R), 4), generator=g, dtype=torch.int32).to(dev)
-    tok_packed = torch.empty((P + N * R, 4), dtype=torch.int32, device=dev)
-    tok_out_packed = torch.zeros((P + N * R,), dtype=torch.float32, device=dev)
-    tok_out_rep = torch.empty((N * (P + R),), dtype=torch.float32, device=dev)
+    tok_rep = torch.randint(0, 2 ** 31 - 1, (T_rep, 4), generator=g, dtype=torch.int32).to(dev)
+    tok_packed = torch.empty((T, 4), dtype=torch.int32, device=dev)
+    tok_out_packed = torch.zeros((T,), dtype=torch.float32, device=dev)
+    tok_out_rep = torch.empty((T_rep,), dtype=torch.float32, device=dev)
 
     o = torch.empty_like(q)
-    lse = torch.empty((Hq, q.shape[0]), dtype=torch.float32, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     dq, dkk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     kw = dict(window=Wn, valid_len=valid)
-    ws = torch.empty(max(256, dk.dualkv_bwd_workspace_bytes(q, k, N, P, R, **kw)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(256, lib_ws(q, k, groups, **kw)), dtype=torch.uint8, device=dev)
 
     def fwd():
-        dk.dualkv_fwd(q, k, v, N, P, R, out=o, lse=lse, **kw)
+        lib_fwd(q, k, v, groups, out=o, lse=lse, **kw)
 
     def bwd():
-        dk.dualkv_bwd(q, k, v, o, lse, do, N, P, R, workspace=ws, dq=dq, dk=dkk, dv=dv, **kw)
+        lib_bwd(q, k, v, o, lse, do, groups, workspace=ws, dq=dq, dk=dkk, dv=dv, **kw)
 
     def step():
-        dk.dualkv_repack(tok_rep, N, P, R, dk.DUALKV_GATHER, out=tok_packed)
+        repack(tok_rep, dk.DUALKV_GATHER, tok_packed)
         fwd()
         bwd()
-        dk.dualkv_repack(tok_out_packed, N, P, R, dk.DUALKV_SCATTER, out=tok_out_rep)
+        repack(tok_out_packed, dk.DUALKV_SCATTER, tok_out_rep)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -176,36 +221,47 @@ def main():
                 "traffic": None if trec is None else trec["bytes_per_launch"]}
 
     # Repack of hidden-state-sized rows (Hq*D bf16 per token), HBM bound.
-    rep_rows = dk.dualkv_repack(do, N, P, R, dk.DUALKV_SCATTER)
+    rep_rows = torch.empty((T_rep,) + tuple(do.shape[1:]), dtype=do.dtype, device=dev)
+    repack(do, dk.DUALKV_SCATTER, rep_rows)
     packed_rows = torch.empty_like(do)
-    ms_gather = timed(lambda: dk.dualkv_repack(rep_rows, N, P, R, dk.DUALKV_GATHER, out=packed_rows), args.steps, torch)
-    ms_scatter = timed(lambda: dk.dualkv_repack(do, N, P, R, dk.DUALKV_SCATTER, out=rep_rows), args.steps, torch)
+    ms_gather = timed(lambda: repack(rep_rows, dk.DUALKV_GATHER, packed_rows), args.steps, torch)
+    ms_scatter = timed(lambda: repack(do, dk.DUALKV_SCATTER, rep_rows), args.steps, torch)
     row_b = Hq * D * do.element_size()
-    gather_gbs = 2 * (P + N * R) * row_b / (ms_gather * 1e-3) / 1e9
-    scatter_gbs = ((P + N * R) + N * (P + R)) * row_b / (ms_scatter * 1e-3) / 1e9
+    gather_gbs = 2 * T * row_b / (ms_gather * 1e-3) / 1e9
+    scatter_gbs = (T + T_rep) * row_b / (ms_scatter * 1e-3) / 1e9
     del rep_rows, packed_rows
 
-    # Same kernels on the replicated layout: N independent causal sequences.
+    # Same kernels on the replicated layout: every group's N sequences as
+    # independent causal sequences (P' = 0, R' = P+R, valid lengths P+L_n).
     rep = None
     if not args.no_replicated:
         print("[bench] replicated layout", file=sys.stderr, flush=True)
-        qr, kr, vr, dor = (dk.dualkv_repack(t, N, P, R, dk.DUALKV_SCATTER) for t in (q, k, v, do))
-        vr_len = torch.tensor([P + l for l in L], dtype=torch.int32, device=dev)
+        rgroups = tuple((N, 0, P + R) for N, P, R in groups)
+
+        def scatter(t):
+            out = torch.empty((T_rep,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+            return repack(t, dk.DUALKV_SCATTER, out)
+
+        qr, kr, vr, dor = (scatter(t) for t in (q, k, v, do))
+        vr_len = torch.tensor([P + l for (N, P, R), L in zip(groups, Ls) for l in L], dtype=torch.int32,
+                              device=dev)
         rkw = dict(window=Wn, valid_len=vr_len)
         orr = torch.empty_like(qr)
         lr = torch.empty((Hq, qr.shape[0]), dtype=torch.float32, device=dev)
         dqr, dkr, dvr = torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(vr)
-        wsr = torch.empty(max(256, dk.dualkv_bwd_workspace_bytes(qr, kr, N, 0, P + R, **rkw)),
-                          dtype=torch.uint8, device=dev)
+        wsr = torch.empty(max(256, lib_ws(qr, kr, rgroups, **rkw)), dtype=torch.uint8, device=dev)
+
+        def rfwd():
+            lib_fwd(qr, kr, vr, rgroups, out=orr, lse=lr, **rkw)
 
         def rstep():
-            dk.dualkv_fwd(qr, kr, vr, N, 0, P + R, out=orr, lse=lr, **rkw)
-            dk.dualkv_bwd(qr, kr, vr, orr, lr, dor, N, 0, P + R, workspace=wsr, dq=dqr, dk=dkr, dv=dvr, **rkw)
+            rfwd()
+            lib_bwd(qr, kr, vr, orr, lr, dor, rgroups, workspace=wsr, dq=dqr, dk=dkr, dv=dvr, **rkw)
 
         rsteps = max(2, args.steps // 2)
         rstep()
         ms_rep = timed(rstep, rsteps, torch)
-        ms_rep_fwd = timed(lambda: dk.dualkv_fwd(qr, kr, vr, N, 0, P + R, out=orr, lse=lr, **rkw), rsteps, torch)
+        ms_rep_fwd = timed(rfwd, rsteps, torch)
         rep = {"ms_fwd_bwd": round(ms_rep, 3), "ms_fwd": round(ms_rep_fwd, 3),
                "tflops_fwd_bwd": round(14 * rep_pairs * Hq * D / (ms_rep * 1e-3) / 1e12, 2),
                "speedup_fwd_bwd": round(ms_rep / (ms_fwd + ms_bwd), 3),
@@ -217,22 +273,26 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        cpu = cpu_baseline(w, groups, x, args.cpu_seconds)
 
     value = fl["fwd_bwd"] / (ms_step * 1e-3) / 1e12
+    config = {"workload": w.name}
+    if grouped:
+        config["groups"] = [list(gr) for gr in groups]
+    else:
+        config.update(N=groups[0][0], P=groups[0][1], R=groups[0][2])
+    config.update(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, window=Wn, packed_tokens=T, replicated_tokens=T_rep)
     line = {
         "metric": "DualKV attn fwd+bwd TFLOP/s, % bf16 MFMA peak, speedup vs replicated layout",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. Gaussian activations of the layer shape)",
-        "config": {"workload": w.name, "N": N, "P": P, "R": R, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "head_dim": D, "window": Wn, "packed_tokens": P + N * R,
-                   "replicated_tokens": N * (P + R)},
+        "config": config,
         "pct_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "fwd": {"ms": round(ms_fwd, 3), "tflops": round(fl["fwd"] / (ms_fwd * 1e-3) / 1e12, 2)},
         "bwd": {"ms": round(ms_bwd, 3), "tflops": round(fl["bwd"] / (ms_bwd * 1e-3) / 1e12, 2)},
-        "rho": round(workcount.token_ratio(N, P, R), 4),
+        "rho": round(T_rep / T, 4),
         "rho_attn": round(rep_pairs / pairs, 4),
         "replicated": rep,
         "kernels": {k_: {kk: round(vv, 4) for kk, vv in d.items()} for k_, d in kernels.items()},

@@ -127,6 +127,64 @@ int dualkv_bwd(const dualkv_params* p, const void* q, const void* k,
                const void* dout, void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Several prompt groups in one call ("DualKV: Shared-Prompt Flash
+ * Attention ..." (arXiv 2605.15422), Abstract: a micro-batch is packed per
+ * prompt; a micro-batch that holds several prompts packs each of them and
+ * lays the packed groups one after the other, as variable-length attention
+ * does with cumulative sequence offsets).
+ *
+ * Group i has its own N_i >= 1 responses of padded length R_i >= 0 sharing
+ * a prompt of P_i >= 0 tokens.  Its T_i = P_i + N_i*R_i packed rows start at
+ * row0_i = T_0 + ... + T_{i-1}; the whole call has Tld = sum_i T_i rows:
+ *   Q, O, dO, dQ  [Tld, Hq, D],  K, V, dK, dV  [Tld, Hkv, D],  LSE [Hq, Tld].
+ * Attention never crosses groups: the rows of group i follow the rules above
+ * with (N_i, P_i, R_i), at positions counted from the group's own row 0.
+ * In dualkv_params, n_resp, prompt_len and resp_len are ignored;
+ * resp_valid_len (device int32, or NULL) holds sum_i N_i entries, group 0's
+ * first.  `groups` is a host array of n_groups entries, 1 <= n_groups <=
+ * DUALKV_MAX_GROUPS (DUALKV_ERR_UNSUPPORTED above, INVALID_ARGUMENT below
+ * or for a malformed entry).  With n_groups = 1 each call is the same as
+ * its single-group counterpart, which is defined as exactly that.
+ * On the MFMA path every kernel of a call covers all groups in one launch
+ * (the launches are those of a single-group call); the scalar path
+ * launches its kernels once per group.  Results per group are bit for bit
+ * those of the single-group call on that group's rows.
+ */
+#define DUALKV_MAX_GROUPS 32
+
+typedef struct dualkv_group {
+  int32_t n_resp;        /* N_i >= 1 */
+  int32_t prompt_len;    /* P_i >= 0 */
+  int32_t resp_len;      /* R_i >= 0 */
+} dualkv_group;
+
+/* dualkv_fwd over groups: o [Tld, Hq, D], lse [Hq, Tld]. */
+int dualkv_fwd_groups(const dualkv_params* p, const dualkv_group* groups,
+                      int32_t n_groups, const void* q, const void* k,
+                      const void* v, void* o, float* lse, void* stream);
+
+/* Workspace of dualkv_bwd_groups for these parameters (0 if invalid). */
+size_t dualkv_bwd_groups_workspace_bytes(const dualkv_params* p,
+                                         const dualkv_group* groups,
+                                         int32_t n_groups);
+
+/* dualkv_bwd over groups, same contract per group (each prompt's dK/dV is
+ * summed over its own queries and its own N_i responses only). */
+int dualkv_bwd_groups(const dualkv_params* p, const dualkv_group* groups,
+                      int32_t n_groups, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* dualkv_repack over groups: the replicated layout holds group after group
+ * (N_i(P_i+R_i) rows each), the packed layout group after group (T_i rows
+ * each); every group is repacked as by dualkv_repack.  Same errors, plus
+ * those of `groups` above. */
+int dualkv_repack_groups(const void* src, void* dst, int64_t row_bytes,
+                         const dualkv_group* groups, int32_t n_groups,
+                         int32_t direction, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* dualkv_strerror(int status);
 

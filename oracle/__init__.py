@@ -20,10 +20,12 @@ the oracle is standard attention written out plainly:
                          sequences, standard attention + its analytic
                          backward per sequence, then the fold of prompt
                          gradients over N (the graded oracle);
-* ``oracle.repack``      the N(P+R) <-> P+NR row maps.
+* ``oracle.repack``      the N(P+R) <-> P+NR row maps;
+* ``oracle.groups``      several prompt groups in one packed micro-batch;
+* ``oracle.rows``        selected rows of the outputs, for full-size checks.
 
 All floating point is fp64.  Parity of every function is pinned by the
 ``-m "not gpu"`` tests (closed forms, library routines, finite
 differences, sum rules); see ``tests/test_oracle_*.py``.
 """
-from . import mask, dense, replicated, repack  # noqa: F401
+from . import mask, dense, replicated, repack, groups  # noqa: F401

@@ -27,13 +27,18 @@ def _f64(a):
 
 def forward(q, k, v, N, P, R, window=0, scale=None, valid_len=None):
     """Return (O [T,Hq,D], LSE [Hq,T]) in fp64."""
+    return forward_masked(q, k, v, visibility(N, P, R, window, valid_len), scale)
+
+
+def forward_masked(q, k, v, vis, scale=None):
+    """Dense attention with an explicit [T, T] visibility mask (query row,
+    key row); returns (O [T,Hq,D], LSE [Hq,T]) in fp64."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    vis = visibility(N, P, R, window, valid_len)
     has = vis.any(axis=1)
     o = np.zeros((T, Hq, D))
     lse = np.full((Hq, T), -np.inf)
@@ -52,13 +57,17 @@ def forward(q, k, v, N, P, R, window=0, scale=None, valid_len=None):
 
 def backward(q, k, v, o, lse, do, N, P, R, window=0, scale=None, valid_len=None):
     """Analytic backward of ``forward``; returns (dQ, dK, dV) in fp64."""
+    return backward_masked(q, k, v, o, lse, do, visibility(N, P, R, window, valid_len), scale)
+
+
+def backward_masked(q, k, v, o, lse, do, vis, scale=None):
+    """Analytic backward of ``forward_masked``; returns (dQ, dK, dV)."""
     q, k, v, o, lse, do = map(_f64, (q, k, v, o, lse, do))
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    vis = visibility(N, P, R, window, valid_len)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)

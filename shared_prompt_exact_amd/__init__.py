@@ -43,6 +43,13 @@ class Params(ctypes.Structure):
     ]
 
 
+class Group(ctypes.Structure):
+    _fields_ = [("n_resp", ctypes.c_int32), ("prompt_len", ctypes.c_int32), ("resp_len", ctypes.c_int32)]
+
+
+MAX_GROUPS = 32
+
+
 def load_library():
     """Load libdualkv.so (once).  Raises if it has not been built."""
     global _lib
@@ -62,6 +69,15 @@ def load_library():
     lib.dualkv_bwd_workspace_bytes.restype = sz
     lib.dualkv_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dualkv_bwd.restype = ctypes.c_int
+    gp = ctypes.POINTER(Group)
+    lib.dualkv_repack_groups.argtypes = [vp, vp, i64, gp, i32, i32, vp]
+    lib.dualkv_repack_groups.restype = ctypes.c_int
+    lib.dualkv_fwd_groups.argtypes = [pp, gp, i32, vp, vp, vp, vp, vp, vp]
+    lib.dualkv_fwd_groups.restype = ctypes.c_int
+    lib.dualkv_bwd_groups_workspace_bytes.argtypes = [pp, gp, i32]
+    lib.dualkv_bwd_groups_workspace_bytes.restype = sz
+    lib.dualkv_bwd_groups.argtypes = [pp, gp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dualkv_bwd_groups.restype = ctypes.c_int
     lib.dualkv_strerror.argtypes = [ctypes.c_int]
     lib.dualkv_strerror.restype = ctypes.c_char_p
     lib.dualkv_profile_start.argtypes = []
@@ -203,3 +219,97 @@ def dualkv_profile_stop():
                "dualkv_profile_kernel")
         out[name.value.decode()] = (int(n.value), float(ms.value))
     return out
+
+
+# ---------------------------------------------------------------- groups
+# `groups` is a sequence of (n_resp, prompt_len, resp_len); the packed rows
+# of the groups follow one another (include/dualkv.h, dualkv_fwd_groups).
+
+def _group_array(groups):
+    gs = [tuple(int(x) for x in g) for g in groups]
+    arr = (Group * max(1, len(gs)))(*[Group(*g) for g in gs])
+    return arr, len(gs), gs
+
+
+def packed_rows(groups) -> int:
+    return sum(P + N * R for N, P, R in groups)
+
+
+def make_group_params(q, k, groups, window=0, softmax_scale=0.0, valid_len=None, impl=IMPL_AUTO) -> Params:
+    T = packed_rows(groups)
+    _require(q, "q")
+    _require(k, "k", dtype=q.dtype)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != T or k.shape[0] != T or q.shape[2] != k.shape[2]:
+        raise ValueError(f"q {tuple(q.shape)} / k {tuple(k.shape)} do not match the groups' {T} rows")
+    if valid_len is not None:
+        _require(valid_len, "valid_len", dtype=torch.int32, shape=(sum(g[0] for g in groups),))
+    return Params(0, 0, 0, q.shape[1], k.shape[1], q.shape[2], window, softmax_scale, _dtype_code(q), impl,
+                  None if valid_len is None else valid_len.data_ptr())
+
+
+def dualkv_repack_groups(src, groups, direction, out=None):
+    """dualkv_repack over groups laid out one after the other."""
+    lib = load_library()
+    arr, n, gs = _group_array(groups)
+    _require(src, "src")
+    rep = sum(N * (P + R) for N, P, R in gs)
+    pk = packed_rows(gs)
+    rows_in, rows_out = (rep, pk) if direction == DUALKV_GATHER else (pk, rep)
+    if src.shape[0] != rows_in:
+        raise ValueError(f"src has {src.shape[0]} rows, expected {rows_in}")
+    if out is None:
+        out = torch.empty((rows_out,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    _require(out, "out", dtype=src.dtype, shape=(rows_out,) + tuple(src.shape[1:]))
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else max(1, src.element_size())
+    _check(lib.dualkv_repack_groups(_ptr(src), _ptr(out), row_bytes, arr, n, direction, _stream()),
+           "dualkv_repack_groups")
+    return out
+
+
+def dualkv_fwd_groups(q, k, v, groups, window=0, softmax_scale=0.0, valid_len=None, impl=IMPL_AUTO,
+                      out=None, lse=None):
+    """Forward over groups; returns (o [Tld,Hq,D], lse [Hq,Tld] fp32)."""
+    lib = load_library()
+    arr, n, gs = _group_array(groups)
+    p = make_group_params(q, k, gs, window, softmax_scale, valid_len, impl)
+    _require(v, "v", dtype=q.dtype, shape=k.shape)
+    T, Hq, _ = q.shape
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(out, "out", dtype=q.dtype, shape=q.shape)
+    _require(lse, "lse", dtype=torch.float32, shape=(Hq, T))
+    _check(lib.dualkv_fwd_groups(ctypes.byref(p), arr, n, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _stream()), "dualkv_fwd_groups")
+    return out, lse
+
+
+def dualkv_bwd_groups_workspace_bytes(q, k, groups, window=0, softmax_scale=0.0, valid_len=None,
+                                      impl=IMPL_AUTO) -> int:
+    arr, n, gs = _group_array(groups)
+    p = make_group_params(q, k, gs, window, softmax_scale, valid_len, impl)
+    return int(load_library().dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), arr, n))
+
+
+def dualkv_bwd_groups(q, k, v, o, lse, dout, groups, window=0, softmax_scale=0.0, valid_len=None,
+                      impl=IMPL_AUTO, workspace=None, dq=None, dk=None, dv=None):
+    """Backward over groups; returns (dq, dk, dv)."""
+    lib = load_library()
+    arr, n, gs = _group_array(groups)
+    p = make_group_params(q, k, gs, window, softmax_scale, valid_len, impl)
+    _require(v, "v", dtype=q.dtype, shape=k.shape)
+    _require(o, "o", dtype=q.dtype, shape=q.shape)
+    _require(dout, "dout", dtype=q.dtype, shape=q.shape)
+    _require(lse, "lse", dtype=torch.float32, shape=(q.shape[1], q.shape[0]))
+    need = int(lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), arr, n))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", dtype=torch.uint8)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, name, dtype=ref.dtype, shape=ref.shape)
+    _check(lib.dualkv_bwd_groups(ctypes.byref(p), arr, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                 _stream()), "dualkv_bwd_groups")
+    return dq, dk, dv

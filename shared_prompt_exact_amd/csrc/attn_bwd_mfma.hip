@@ -26,6 +26,8 @@
 // The prompt K/V tile is thereby reused by the query blocks of all N
 // responses inside one workgroup, and the N-fold sum never leaves a fixed
 // order, so results are bitwise reproducible.
+#include <algorithm>
+
 #include "lds_tiles.h"
 
 namespace dualkv {
@@ -62,7 +64,7 @@ struct DqCfg {
 // dP meet in LDS and are summed in the same order by both waves.
 template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
-    bwd_dq_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
+    bwd_dq_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   const uint16_t* __restrict__ dout, const float* __restrict__ lse,
                   const float* __restrict__ delta, uint16_t* __restrict__ dq) {
@@ -75,10 +77,24 @@ __global__ void __launch_bounds__(NW * 64)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dh = wave % DS, wq = wave / DS;
   const int BM = 32 * NWQ / HG;
-  const int NB = nbP + pr.N * nbR;
-  const int L = balanced_block(blockIdx.x, pr.Hq / HG, NB);
+  const int NB = GB.off[G.n];                 // row blocks of all groups, per head group
+  const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;                          // grid padding (whole workgroup)
-  const int hgi = L / NB, blk = L % NB;
+  const int hgi = L / NB;
+  const int gi = group_of(GB.off, G.n, L % NB);
+  const int blk = L % NB - GB.off[gi];
+  const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    dout += r0 * pr.Hq * D;
+    dq += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    lse += r0;
+    delta += r0;
+  }
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
   const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
@@ -109,9 +125,9 @@ __global__ void __launch_bounds__(NW * 64)
   }
   float lse2 = INFINITY, dlt = 0.f;   // +inf: p = 0 for rows without keys
   if (qvalid) {
-    const float Lr = lse[(int64_t)h * pr.T + qrow];
+    const float Lr = lse[(int64_t)h * pr.Tld + qrow];
     lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
-    dlt = delta[(int64_t)h * pr.T + qrow];
+    dlt = delta[(int64_t)h * pr.Tld + qrow];
   }
   wait_vmcnt<0>();                    // the loop's waits count only tile loads
   asm volatile("" ::: "memory");
@@ -317,6 +333,15 @@ struct KvShape {
   int t0;             // first prompt tile a response query can see (window)
 };
 
+// Work items of the dK/dV kernel per prompt group: group i owns items
+// [off[i], off[i+1]) of every KV head, has key tiling sh[i] and writes its
+// prompt partials from float part[i] of the partial buffers.
+struct KvGroups {
+  int off[kMaxGroups + 1];
+  KvShape sh[kMaxGroups];
+  int64_t part[kMaxGroups];
+};
+
 // Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
 // positions) of the item; lo is rounded down to a stage boundary.
 __device__ __forceinline__ void seg_rows(const Problem& pr, int seg, int kp_lo, int kp_hi, int& lo,
@@ -371,7 +396,7 @@ __device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int k
 // feeds two MFMAs.
 template <int D, int NWK, int NS, int DS, bool VREG, int KW>
 __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, KW == 2 ? 1 : 8)))
-    bwd_dkdv_kernel(Problem pr, KvShape sh, const uint16_t* __restrict__ q,
+    bwd_dkdv_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk,
@@ -384,13 +409,31 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- decode the work item (longest first within a KV head)
-  const int per_head = (sh.nPt - sh.t0) * (sh.slots - 1) + sh.nPt + pr.N * sh.nRt;
-  const int Lid = balanced_block(blockIdx.x, pr.Hkv, per_head);
+  // ---- decode the work item (groups in order, longest first within a
+  // group and KV head)
+  const int per_head = KG.off[G.n];
+  const int Lid = balanced_block(blockIdx.x, pa.Hkv, per_head);
   if (Lid < 0) return;                        // grid padding (whole workgroup)
   KvItem it;
   it.c = Lid / per_head;
   int x = Lid % per_head;
+  const int gi = group_of(KG.off, G.n, x);
+  x -= KG.off[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  const KvShape sh = KG.sh[gi];
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    dout += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    dk += r0 * pr.Hkv * D;
+    dv += r0 * pr.Hkv * D;
+    lse2 += r0;
+    delta += r0;
+    part_k += KG.part[gi];
+    part_v += KG.part[gi];
+  }
   // response slots exist only for prompt tiles t0 .. nPt-1 (all of them
   // without a window)
   const int nPtR = sh.nPt - sh.t0;
@@ -509,7 +552,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
     if (stat_wave) {
       // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
       const int row = sb + st.r + min(lane & 31, n - 1);
-      const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.T + row;
+      const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.Tld + row;
       const unsigned ldsaddr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
           __attribute__((address_space(3))) void*)(buf + C::Q_ELEMS + C::DO_ELEMS));
       asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
@@ -737,7 +780,7 @@ __global__ void __launch_bounds__(256)
   constexpr int G = D / 8;                  // lanes per row
   constexpr int RPW = 64 / G;               // rows per wave
   const int lane = threadIdx.x & 63, sub = lane % G;
-  const int64_t nrows = (int64_t)pr.T * pr.Hq;
+  const int64_t nrows = (int64_t)pr.Tld * pr.Hq;   // every row of the launch
   const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
   float acc = 0.f;
   if (row < nrows) {
@@ -754,7 +797,7 @@ __global__ void __launch_bounds__(256)
   for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < nrows && sub == 0) {
     const int t = (int)(row / pr.Hq), h = (int)(row % pr.Hq);
-    const int64_t at = (int64_t)h * pr.T + t;
+    const int64_t at = (int64_t)h * pr.Tld + t;
     const float L = lse[at];
     delta[at] = L == -INFINITY ? 0.f : acc;
     lse2[at] = L == -INFINITY ? INFINITY : L * kLog2e;
@@ -763,12 +806,25 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------ slot reduction
 
-// Prompt rows whose key tiles wrote per-slot fp32 partials: float4 index
-// i0 .. i0+n4-1 of the [P, Hkv, D] prompt block (slot stride `stride4`).
+// Per prompt group (blockIdx.y): prompt rows whose key tiles wrote
+// per-slot fp32 partials, float4 index i0 .. i0+n4-1 of the group's
+// [P, Hkv, D] prompt block (from float4 part4 of the partial buffers, slot
+// stride `stride4`); the sums go to dK/dV from 4-element index out4.
+struct RedGroups {
+  int slots[kMaxGroups];
+  int64_t part4[kMaxGroups], stride4[kMaxGroups], i0[kMaxGroups], n4[kMaxGroups], out4[kMaxGroups];
+};
+
 __global__ void __launch_bounds__(256)
-    reduce_slots_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v,
-                        int slots, int64_t stride4, int64_t i0, int64_t n4, uint16_t* __restrict__ dk,
-                        uint16_t* __restrict__ dv) {
+    reduce_slots_kernel(const float* __restrict__ part_k, const float* __restrict__ part_v, RedGroups RG,
+                        uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  const int gi = blockIdx.y;
+  const int slots = RG.slots[gi];
+  const int64_t stride4 = RG.stride4[gi], i0 = RG.i0[gi], n4 = RG.n4[gi];
+  part_k += 4 * RG.part4[gi];
+  part_v += 4 * RG.part4[gi];
+  dk += 4 * RG.out4[gi];
+  dv += 4 * RG.out4[gi];
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n4;
        j += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = i0 + j;
@@ -807,58 +863,100 @@ inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
 inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
 struct BwdPlan {
-  int NW, DS, HG, BM, nbP, nbR;
+  int NW, DS, HG, BM;
+  GroupBlocks gb;          // dQ row blocks per group
   int64_t nwg_dq;
-  KvShape sh;
+  KvGroups kg;             // dK/dV items per group
+  RedGroups rg;            // slot reduction per group
   int BK;
   int64_t nwg_kv;
+  int64_t red_blocks;      // reduction workgroups per group (grid.x)
+  bool reduce;             // some group has response slots
   size_t off_delta, off_lse2, off_pk, off_pv, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdPlan plan(const Problem& pr) {
+// Key tiling of one group's dK/dV work.
+KvShape kv_shape(int N, int P, int R, int W, int BK) {
+  KvShape sh;
+  sh.nPt = (P + BK - 1) / BK;
+  sh.nRt = (R + BK - 1) / BK;
+  // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
+  // most P of them); the responses are cut into ranges of about P queries
+  // each, so no slot is much longer than the longest prompt slot.
+  int rslots = 0;
+  if (P > 0 && R > 0) {
+    const int64_t nr = (int64_t)N * R;
+    rslots = (int)((nr + P - 1) / P);
+    rslots = max(1, min(rslots, N));
+  }
+  sh.per_slot = rslots > 0 ? (N + rslots - 1) / rslots : 1;
+  if (rslots > 0) rslots = (N + sh.per_slot - 1) / sh.per_slot;
+  sh.slots = 1 + rslots;
+  // With a window, response query r (position P + r) sees prompt keys from
+  // P + r - W + 1 on, so prompt keys below P - W + 1 get no response term.
+  const int first_seen = W > 0 ? max(0, P - W + 1) : 0;
+  sh.t0 = rslots > 0 ? min(sh.nPt, first_seen / BK) : sh.nPt;
+  return sh;
+}
+
+BwdPlan plan(const Problem& pr, const Groups& G) {
   BwdPlan p;
   p.NW = dq_waves(pr.D);
   p.DS = dq_split(pr.D);
   p.HG = heads_per_block(pr.g, p.NW / p.DS);
   p.BM = 32 * (p.NW / p.DS) / p.HG;
-  p.nbP = (pr.P + p.BM - 1) / p.BM;
-  p.nbR = (pr.R + p.BM - 1) / p.BM;
-  p.nwg_dq = balanced_grid(pr.Hq / p.HG, p.nbP + (int64_t)pr.N * p.nbR);
   const int BK = 32 * kv_tiles_per_wave(pr.D) * kv_waves(pr.D) / kv_split(pr.D);
-  p.sh.nPt = (pr.P + BK - 1) / BK;
-  p.sh.nRt = (pr.R + BK - 1) / BK;
-  // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
-  // most P of them); the responses are cut into ranges of about P queries
-  // each, so no slot is much longer than the longest prompt slot.
-  int rslots = 0;
-  if (pr.P > 0 && pr.R > 0) {
-    const int64_t nr = (int64_t)pr.N * pr.R;
-    rslots = (int)((nr + pr.P - 1) / pr.P);
-    rslots = max(1, min(rslots, pr.N));
-  }
-  p.sh.per_slot = rslots > 0 ? (pr.N + rslots - 1) / rslots : 1;
-  if (rslots > 0) rslots = (pr.N + p.sh.per_slot - 1) / p.sh.per_slot;
-  p.sh.slots = 1 + rslots;
-  // With a window, response query r (position P + r) sees prompt keys from
-  // P + r - W + 1 on, so prompt keys below P - W + 1 get no response term.
-  const int first_seen = pr.W > 0 ? max(0, pr.P - pr.W + 1) : 0;
-  p.sh.t0 = rslots > 0 ? min(p.sh.nPt, first_seen / BK) : p.sh.nPt;
-  p.nwg_kv = balanced_grid(pr.Hkv, (int64_t)(p.sh.nPt - p.sh.t0) * (p.sh.slots - 1) + p.sh.nPt +
-                                       (int64_t)pr.N * p.sh.nRt);
   p.BK = BK;
+  constexpr int64_t kBig = INT32_MAX;
+  int64_t nb = 0, items = 0, part = 0, red = 0;
+  p.reduce = false;
+  for (int i = 0; i < G.n; ++i) {
+    const int N = G.N[i], P = G.P[i], R = G.R[i];
+    p.gb.off[i] = (int)std::min(nb, kBig);
+    p.gb.nbP[i] = (P + p.BM - 1) / p.BM;
+    p.gb.nbR[i] = (R + p.BM - 1) / p.BM;
+    nb += p.gb.nbP[i] + (int64_t)N * p.gb.nbR[i];
+
+    const KvShape sh = kv_shape(N, P, R, pr.W, BK);
+    p.kg.sh[i] = sh;
+    p.kg.off[i] = (int)std::min(items, kBig);
+    items += (int64_t)(sh.nPt - sh.t0) * (sh.slots - 1) + sh.nPt + (int64_t)N * sh.nRt;
+    // fp32 partials [slots, P, Hkv, D] of this group, 256-byte aligned
+    p.kg.part[i] = part;
+    const int64_t row4 = (int64_t)pr.Hkv * pr.D / 4;   // float4s per prompt row
+    p.rg.slots[i] = sh.slots;
+    p.rg.part4[i] = part / 4;
+    p.rg.stride4[i] = (int64_t)P * row4;
+    p.rg.out4[i] = (int64_t)G.row0[i] * row4;
+    if (sh.slots > 1 && sh.t0 < sh.nPt) {
+      // prompt rows t0*BK .. P-1: the rows whose tiles wrote slot partials
+      const int64_t r0 = (int64_t)sh.t0 * BK;
+      p.rg.i0[i] = r0 * row4;
+      p.rg.n4[i] = (P - r0) * row4;
+      p.reduce = true;
+      red = std::max(red, p.rg.n4[i]);
+      part += (int64_t)align256((size_t)sh.slots * P * pr.Hkv * pr.D * sizeof(float)) / 4;
+    } else {
+      p.rg.i0[i] = p.rg.n4[i] = 0;
+    }
+  }
+  p.gb.off[G.n] = (int)std::min(nb, kBig);
+  p.kg.off[G.n] = (int)std::min(items, kBig);
+  p.nwg_dq = nb >= kBig ? ((int64_t)1 << 40) : balanced_grid(pr.Hq / p.HG, nb);
+  p.nwg_kv = items >= kBig ? ((int64_t)1 << 40) : balanced_grid(pr.Hkv, items);
+  p.red_blocks = std::min<int64_t>(std::max<int64_t>((red + 255) / 256, 1), std::max(1, 4096 / G.n));
   p.off_delta = 0;
-  p.off_lse2 = align256((size_t)pr.Hq * pr.T * sizeof(float));
+  p.off_lse2 = align256((size_t)pr.Hq * pr.Tld * sizeof(float));
   p.off_pk = 2 * p.off_lse2;
-  const size_t part = p.sh.slots > 1 ? align256((size_t)p.sh.slots * pr.P * pr.Hkv * pr.D * sizeof(float)) : 0;
-  p.off_pv = p.off_pk + part;
-  p.bytes = p.off_pv + part;
+  p.off_pv = p.off_pk + (size_t)part * sizeof(float);
+  p.bytes = p.off_pv + (size_t)part * sizeof(float);
   return p;
 }
 
 template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG, int KW>
-hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k, const void* v,
+hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void* q, const void* k, const void* v,
                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                char* ws, hipStream_t stream) {
   using CQ = DqCfg<D, kDqBN, NW, DQNS, DS>;
@@ -879,33 +977,26 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
   hipError_t e;
   {
     constexpr int RPB = 4 * 64 / (D / 8);   // rows per 256-thread block
-    const int64_t nrows = (int64_t)pr.T * pr.Hq;
+    const int64_t nrows = (int64_t)pr.Tld * pr.Hq;
     e = launch("bwd_delta", delta_lse2_kernel<D>, dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0,
                stream, pr, static_cast<const uint16_t*>(o), do16, lse, delta, lse2);
     if (e != hipSuccess) return e;
   }
   if (p.nwg_dq > 0) {
     e = launch("bwd_dq", bwd_dq_kernel<D, kDqBN, NW, DQNS, DS>, dim3((unsigned)p.nwg_dq), dim3(NW * 64), CQ::LDS_BYTES,
-               stream, pr, p.HG, p.nbP, p.nbR, q16, k16, v16, do16, lse, delta,
+               stream, pr, G, p.gb, p.HG, q16, k16, v16, do16, lse, delta,
                static_cast<uint16_t*>(dq));
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
     e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
-               stream, pr, p.sh, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
+               stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
   }
-  if (p.sh.slots > 1 && p.sh.t0 < p.sh.nPt) {
-    // prompt rows t0*BK .. P-1: the rows whose tiles wrote slot partials
-    const int64_t r0 = (int64_t)p.sh.t0 * p.BK;
-    const int64_t row4 = (int64_t)pr.Hkv * D / 4;        // float4s per prompt row
-    const int64_t n4 = (pr.P - r0) * row4;
-    int64_t blocks = (n4 + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    e = launch("bwd_reduce", reduce_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pk, pv,
-               p.sh.slots, (int64_t)pr.P * row4, r0 * row4, n4, static_cast<uint16_t*>(dk),
-               static_cast<uint16_t*>(dv));
+  if (p.reduce) {
+    e = launch("bwd_reduce", reduce_slots_kernel, dim3((unsigned)p.red_blocks, (unsigned)G.n), dim3(256), 0,
+               stream, pk, pv, p.rg, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -913,25 +1004,25 @@ hipError_t run(const Problem& pr, const BwdPlan& p, const void* q, const void* k
 
 }  // namespace
 
-bool bwd_mfma_supported(const Problem& pr) {
+bool bwd_mfma_supported(const Problem& pr, const Groups& G) {
   if (pr.D != 64 && pr.D != 128 && pr.D != 256 && pr.D != 512) return false;
-  const BwdPlan p = plan(pr);
+  const BwdPlan p = plan(pr, G);
   return p.nwg_dq < ((int64_t)1 << 31) && p.nwg_kv < ((int64_t)1 << 31);
 }
 
-size_t bwd_mfma_workspace_bytes(const Problem& pr) { return plan(pr).bytes; }
+size_t bwd_mfma_workspace_bytes(const Problem& pr, const Groups& G) { return plan(pr, G).bytes; }
 
-hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
-                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, void* workspace, hipStream_t stream) {
-  const BwdPlan p = plan(pr);
+hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, void* workspace, hipStream_t stream) {
+  const BwdPlan p = plan(pr, G);
   char* ws = static_cast<char*>(workspace);
   switch (pr.D) {
     //                D  NW NWK BN DQNS KVNS DS KDS VREG KW
-    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,6 +29,8 @@
 //    2^8 (the softmax is exact for any reference max);
 //  * workgroups are ordered longest key range first and mapped so each XCD
 //    works on one head group at a time with an equal share of the work.
+#include <algorithm>
+
 #include "lds_tiles.h"
 
 namespace dualkv {
@@ -67,7 +69,7 @@ struct FwdCfg {
 // the same order by both so they agree bit for bit.
 template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
-    fwd_mfma_kernel(Problem pr, int HG, int nbP, int nbR, const uint16_t* __restrict__ q,
+    fwd_mfma_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     uint16_t* __restrict__ o, float* __restrict__ lse) {
   using C = FwdCfg<D, BN, NW, NS, DS>;
@@ -79,10 +81,23 @@ __global__ void __launch_bounds__(NW * 64)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dh = wave % DS, wq = wave / DS;     // head-dim half, query slot
   const int BM = 32 * NWQ / HG;
-  const int NB = nbP + pr.N * nbR;
-  const int L = balanced_block(blockIdx.x, pr.Hq / HG, NB);
+  const int NB = GB.off[G.n];                   // row blocks of all groups, per head group
+  const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;                            // grid padding (whole workgroup)
-  const int hgi = L / NB, blk = L % NB;
+  const int hgi = L / NB;
+  // the prompt group of this block; rows and statistics below are the group's
+  const int gi = group_of(GB.off, G.n, L % NB);
+  const int blk = L % NB - GB.off[gi];
+  const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    o += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    lse += r0;
+  }
   const int gpw = pr.g / HG;
   const int c = hgi / gpw;
   const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
@@ -289,16 +304,17 @@ __global__ void __launch_bounds__(NW * 64)
         *reinterpret_cast<uint2*>(orow + d) = pk.u;
       }
     if (hf == 0 && dh == 0)
-      lse[(int64_t)h * pr.T + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+      lse[(int64_t)h * pr.Tld + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
 
 struct FwdPlan {
-  int NW, BN, DS, HG, BM, nbP, nbR;
+  int NW, BN, DS, HG, BM;
+  GroupBlocks gb;
   int64_t nwg;
 };
 
-FwdPlan plan(const Problem& pr) {
+FwdPlan plan(const Problem& pr, const Groups& G) {
   FwdPlan p;
   // Per wave, Q^T and the O accumulator take 3*D/4 registers: two waves per
   // SIMD fit up to D = 128; D = 256 splits the head dim over wave pairs
@@ -308,42 +324,48 @@ FwdPlan plan(const Problem& pr) {
   p.DS = pr.D <= 128 ? 1 : 2;
   p.HG = heads_per_block(pr.g, p.NW / p.DS);
   p.BM = 32 * (p.NW / p.DS) / p.HG;
-  p.nbP = (pr.P + p.BM - 1) / p.BM;
-  p.nbR = (pr.R + p.BM - 1) / p.BM;
-  p.nwg = balanced_grid(pr.Hq / p.HG, p.nbP + (int64_t)pr.N * p.nbR);
+  int64_t nb = 0;
+  for (int i = 0; i < G.n; ++i) {
+    p.gb.off[i] = (int)std::min<int64_t>(nb, INT32_MAX);
+    p.gb.nbP[i] = (G.P[i] + p.BM - 1) / p.BM;
+    p.gb.nbR[i] = (G.R[i] + p.BM - 1) / p.BM;
+    nb += p.gb.nbP[i] + (int64_t)G.N[i] * p.gb.nbR[i];
+  }
+  p.gb.off[G.n] = (int)std::min<int64_t>(nb, INT32_MAX);
+  p.nwg = nb >= INT32_MAX ? ((int64_t)1 << 40) : balanced_grid(pr.Hq / p.HG, nb);
   return p;
 }
 
 template <int D, int BN, int NW, int NS, int DS>
-hipError_t run(const Problem& pr, const FwdPlan& p, const void* q, const void* k, const void* v,
+hipError_t run(const Problem& pr, const Groups& G, const FwdPlan& p, const void* q, const void* k, const void* v,
                void* o, float* lse, hipStream_t stream) {
   using C = FwdCfg<D, BN, NW, NS, DS>;
   static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
   static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   return launch("fwd", fwd_mfma_kernel<D, BN, NW, NS, DS>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
-                stream, pr, p.HG, p.nbP, p.nbR, static_cast<const uint16_t*>(q),
+                stream, pr, G, p.gb, p.HG, static_cast<const uint16_t*>(q),
                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                 static_cast<uint16_t*>(o), lse);
 }
 
 }  // namespace
 
-bool fwd_mfma_supported(const Problem& pr) {
+bool fwd_mfma_supported(const Problem& pr, const Groups& G) {
   if (pr.D != 64 && pr.D != 128 && pr.D != 256 && pr.D != 512) return false;
-  const FwdPlan p = plan(pr);
+  const FwdPlan p = plan(pr, G);
   return p.nwg < ((int64_t)1 << 31);
 }
 
-hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, const void* v, void* o,
-                           float* lse, hipStream_t stream) {
-  const FwdPlan p = plan(pr);
+hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, const void* k,
+                           const void* v, void* o, float* lse, hipStream_t stream) {
+  const FwdPlan p = plan(pr, G);
   if (p.nwg == 0) return hipSuccess;
   switch (pr.D) {
-    case 64: return run<64, 64, 8, 3, 1>(pr, p, q, k, v, o, lse, stream);
-    case 128: return run<128, 64, 8, 3, 1>(pr, p, q, k, v, o, lse, stream);
-    case 256: return run<256, 32, 8, 3, 2>(pr, p, q, k, v, o, lse, stream);
-    case 512: return run<512, 32, 4, 2, 2>(pr, p, q, k, v, o, lse, stream);   // 64 KiB per slot
+    case 64: return run<64, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
+    case 128: return run<128, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
+    case 256: return run<256, 32, 8, 3, 2>(pr, G, p, q, k, v, o, lse, stream);
+    case 512: return run<512, 32, 4, 2, 2>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
 }

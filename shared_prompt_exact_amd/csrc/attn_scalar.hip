@@ -14,6 +14,8 @@
 // responses ascending), so results are deterministic without atomics.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dualkv {
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(256) fwd_scalar_kernel(Problem pr, const T* __
     const int d = lane + 64 * i;
     if (d < D) Elem<T>::store(o + qoff + d, acc[i] * inv);
   }
-  if (lane == 0) lse[(int64_t)h * pr.T + t] = has ? m + logf(l) : -INFINITY;
+  if (lane == 0) lse[(int64_t)h * pr.Tld + t] = has ? m + logf(l) : -INFINITY;
 }
 
 template <typename T>
@@ -127,14 +129,14 @@ __global__ void __launch_bounds__(256) delta_kernel(Problem pr, const T* __restr
                                                     float* __restrict__ delta) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-  if (item >= (int64_t)pr.T * pr.Hq) return;
+  if (item >= (int64_t)pr.Tld * pr.Hq) return;        // every row of the launch
   const int t = (int)(item / pr.Hq), h = (int)(item % pr.Hq);
   const int64_t off = ((int64_t)t * pr.Hq + h) * pr.D;
   float s = 0.f;
   for (int d = lane; d < pr.D; d += 64) s = fmaf(Elem<T>::load(dout + off + d), Elem<T>::load(o + off + d), s);
   s = wave_sum(s);
-  const float L = lse[(int64_t)h * pr.T + t];
-  if (lane == 0) delta[(int64_t)h * pr.T + t] = L == -INFINITY ? 0.f : s;
+  const float L = lse[(int64_t)h * pr.Tld + t];
+  if (lane == 0) delta[(int64_t)h * pr.Tld + t] = L == -INFINITY ? 0.f : s;
 }
 
 template <typename T>
@@ -161,8 +163,8 @@ __global__ void __launch_bounds__(256) dq_scalar_kernel(Problem pr, const T* __r
   __syncthreads();
   if (!active) return;
   KeyRanges kr = keys_of_query(pr, t);
-  const float L = lse[(int64_t)h * pr.T + t];
-  const float Dl = delta[(int64_t)h * pr.T + t];
+  const float L = lse[(int64_t)h * pr.Tld + t];
+  const float Dl = delta[(int64_t)h * pr.Tld + t];
   float acc[kDpl];
 #pragma unroll
   for (int i = 0; i < kDpl; ++i) acc[i] = 0.f;
@@ -269,8 +271,8 @@ __global__ void __launch_bounds__(256) dkdv_scalar_kernel(Problem pr, const T* _
             sdot = fmaf(Elem<T>::load(qp + d), ks[wave][d], sdot);
             pdot = fmaf(Elem<T>::load(dp + d), vs[wave][d], pdot);
           }
-          p = expf(sdot * pr.scale - lse[(int64_t)h * pr.T + i]);
-          ds = p * (pdot - delta[(int64_t)h * pr.T + i]);
+          p = expf(sdot * pr.scale - lse[(int64_t)h * pr.Tld + i]);
+          ds = p * (pdot - delta[(int64_t)h * pr.Tld + i]);
         }
         const int cnt = min(64, s1 - base);
         for (int ii = 0; ii < cnt; ++ii) {
@@ -301,21 +303,47 @@ __global__ void __launch_bounds__(256) dkdv_scalar_kernel(Problem pr, const T* _
 
 unsigned blocks_for(int64_t items) { return (unsigned)((items + kWaves - 1) / kWaves); }
 
+// Byte offset of packed row `row` in a [rows, H, D] tensor.
+int64_t row_bytes_at(int64_t row, int H, int D, int dtype) {
+  return row * H * D * (dtype == DUALKV_F32 ? 4 : 2);
+}
+template <typename T>
+T* at(T* p, int64_t bytes) {
+  using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+  return reinterpret_cast<T*>(reinterpret_cast<B*>(p) + bytes);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
-                             const void* v, void* o, float* lse, hipStream_t stream) {
-  const dim3 grid(blocks_for((int64_t)pr.T * pr.Hq)), block(64 * kWaves);
-  if (dtype == DUALKV_F32)
-    return launch("fwd_scalar", fwd_scalar_kernel<float>, grid, block, 0, stream, pr, (const float*)q,
-                  (const float*)k, (const float*)v, (float*)o, lse);
-  return launch("fwd_scalar", fwd_scalar_kernel<uint16_t>, grid, block, 0, stream, pr, (const uint16_t*)q,
-                (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse);
+// One launch per prompt group (the scalar path is the exactness path, not
+// a fast one); each group's tensors and [H, Tld] rows are offset to its row 0.
+hipError_t launch_fwd_scalar(const Problem& pr, const Groups& G, int dtype, const void* q,
+                             const void* k, const void* v, void* o, float* lse, hipStream_t stream) {
+  for (int gi = 0; gi < G.n; ++gi) {
+    const Problem gp = group_problem(pr, G, gi);
+    if (gp.T == 0) continue;
+    const int64_t r0 = G.row0[gi];
+    const void* qg = at(q, row_bytes_at(r0, pr.Hq, pr.D, dtype));
+    const void* kg = at(k, row_bytes_at(r0, pr.Hkv, pr.D, dtype));
+    const void* vg = at(v, row_bytes_at(r0, pr.Hkv, pr.D, dtype));
+    void* og = at(o, row_bytes_at(r0, pr.Hq, pr.D, dtype));
+    float* lg = lse + r0;
+    const dim3 grid(blocks_for((int64_t)gp.T * pr.Hq)), block(64 * kWaves);
+    hipError_t e;
+    if (dtype == DUALKV_F32)
+      e = launch("fwd_scalar", fwd_scalar_kernel<float>, grid, block, 0, stream, gp, (const float*)qg,
+                 (const float*)kg, (const float*)vg, (float*)og, lg);
+    else
+      e = launch("fwd_scalar", fwd_scalar_kernel<uint16_t>, grid, block, 0, stream, gp, (const uint16_t*)qg,
+                 (const uint16_t*)kg, (const uint16_t*)vg, (uint16_t*)og, lg);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const void* dout,
                             const float* lse, float* delta, hipStream_t stream) {
-  const dim3 grid(blocks_for((int64_t)pr.T * pr.Hq)), block(64 * kWaves);
+  const dim3 grid(blocks_for((int64_t)pr.Tld * pr.Hq)), block(64 * kWaves);
   if (dtype == DUALKV_F32)
     return launch("bwd_delta", delta_kernel<float>, grid, block, 0, stream, pr, (const float*)o,
                   (const float*)dout, lse, delta);
@@ -323,28 +351,41 @@ hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const v
                 (const uint16_t*)dout, lse, delta);
 }
 
-hipError_t launch_bwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
-                             const void* v, const void* o, const float* lse, const void* dout,
-                             void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
+hipError_t launch_bwd_scalar(const Problem& pr, const Groups& G, int dtype, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* delta,
+                             hipStream_t stream) {
   hipError_t e = launch_bwd_delta(pr, dtype, o, dout, lse, delta, stream);
   if (e != hipSuccess) return e;
-  const dim3 gq(blocks_for((int64_t)pr.T * pr.Hq)), gk(blocks_for((int64_t)pr.T * pr.Hkv));
   const dim3 block(64 * kWaves);
-  if (dtype == DUALKV_F32) {
-    e = launch("bwd_dq_scalar", dq_scalar_kernel<float>, gq, block, 0, stream, pr, (const float*)q, (const float*)k,
-               (const float*)v, (const float*)dout, lse, (const float*)delta, (float*)dq);
+  for (int gi = 0; gi < G.n; ++gi) {
+    const Problem gp = group_problem(pr, G, gi);
+    if (gp.T == 0) continue;
+    const int64_t r0 = G.row0[gi];
+    const int64_t bq = row_bytes_at(r0, pr.Hq, pr.D, dtype), bk = row_bytes_at(r0, pr.Hkv, pr.D, dtype);
+    const dim3 gq(blocks_for((int64_t)gp.T * pr.Hq)), gk(blocks_for((int64_t)gp.T * pr.Hkv));
+    const float* lg = lse + r0;
+    const float* dg = delta + r0;
+    if (dtype == DUALKV_F32) {
+      e = launch("bwd_dq_scalar", dq_scalar_kernel<float>, gq, block, 0, stream, gp, at((const float*)q, bq),
+                 at((const float*)k, bk), at((const float*)v, bk), at((const float*)dout, bq), lg, dg,
+                 at((float*)dq, bq));
+      if (e != hipSuccess) return e;
+      e = launch("bwd_dkdv_scalar", dkdv_scalar_kernel<float>, gk, block, 0, stream, gp, at((const float*)q, bq),
+                 at((const float*)k, bk), at((const float*)v, bk), at((const float*)dout, bq), lg, dg,
+                 at((float*)dk, bk), at((float*)dv, bk));
+    } else {
+      e = launch("bwd_dq_scalar", dq_scalar_kernel<uint16_t>, gq, block, 0, stream, gp,
+                 at((const uint16_t*)q, bq), at((const uint16_t*)k, bk), at((const uint16_t*)v, bk),
+                 at((const uint16_t*)dout, bq), lg, dg, at((uint16_t*)dq, bq));
+      if (e != hipSuccess) return e;
+      e = launch("bwd_dkdv_scalar", dkdv_scalar_kernel<uint16_t>, gk, block, 0, stream, gp,
+                 at((const uint16_t*)q, bq), at((const uint16_t*)k, bk), at((const uint16_t*)v, bk),
+                 at((const uint16_t*)dout, bq), lg, dg, at((uint16_t*)dk, bk), at((uint16_t*)dv, bk));
+    }
     if (e != hipSuccess) return e;
-    return launch("bwd_dkdv_scalar", dkdv_scalar_kernel<float>, gk, block, 0, stream, pr, (const float*)q,
-                  (const float*)k, (const float*)v, (const float*)dout, lse, (const float*)delta,
-                  (float*)dk, (float*)dv);
   }
-  e = launch("bwd_dq_scalar", dq_scalar_kernel<uint16_t>, gq, block, 0, stream, pr, (const uint16_t*)q,
-             (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
-             (const float*)delta, (uint16_t*)dq);
-  if (e != hipSuccess) return e;
-  return launch("bwd_dkdv_scalar", dkdv_scalar_kernel<uint16_t>, gk, block, 0, stream, pr, (const uint16_t*)q,
-                (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
-                (const float*)delta, (uint16_t*)dk, (uint16_t*)dv);
+  return hipSuccess;
 }
 
 }  // namespace dualkv

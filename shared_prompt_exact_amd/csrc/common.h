@@ -10,16 +10,55 @@
 
 namespace dualkv {
 
-// Validated problem description passed by value to every kernel.
+// Validated problem description passed by value to every kernel.  In a
+// launch over several prompt groups, N, P, R, T and valid_len describe one
+// group (the kernels derive them per workgroup, see group_problem) and Tld
+// counts the rows of all groups: LSE, Delta and their kin are [H, Tld].
 struct Problem {
   int N, P, R;          // responses, prompt length, padded response length
   int Hq, Hkv, D;       // heads and head dim
   int g;                // Hq / Hkv
   int W;                // window (<= 0: none)
   int T;                // P + N*R packed rows
+  int Tld;              // rows of the whole launch (leading dim of [H, rows] arrays)
   float scale;          // softmax scale (> 0)
   const int32_t* valid_len;  // device [N] or nullptr
 };
+
+// Prompt groups of one launch.  Group i holds packed rows row0[i] ..
+// row0[i] + P[i] + N[i]*R[i] - 1 (its own prompt, then its N[i] responses),
+// and its valid lengths start at entry vl0[i] of the launch's array.
+constexpr int kMaxGroups = 32;
+struct Groups {
+  int n;
+  int N[kMaxGroups], P[kMaxGroups], R[kMaxGroups];
+  int row0[kMaxGroups], vl0[kMaxGroups];
+};
+
+// The problem of group gi (rows relative to the group's row 0).
+__host__ __device__ inline Problem group_problem(const Problem& base, const Groups& G, int gi) {
+  Problem p = base;
+  p.N = G.N[gi];
+  p.P = G.P[gi];
+  p.R = G.R[gi];
+  p.T = p.P + p.N * p.R;
+  p.valid_len = base.valid_len ? base.valid_len + G.vl0[gi] : nullptr;
+  return p;
+}
+
+// Logical blocks of a launch per group: group i owns [off[i], off[i+1]).
+struct GroupBlocks {
+  int off[kMaxGroups + 1];
+  int nbP[kMaxGroups], nbR[kMaxGroups];   // prompt / response row blocks (query-parallel kernels)
+};
+
+// Group of logical block x (a linear scan: at most kMaxGroups entries,
+// scalar registers only).
+__device__ __forceinline__ int group_of(const int* off, int n, int x) {
+  int gi = 0;
+  while (gi + 1 < n && x >= off[gi + 1]) ++gi;
+  return gi;
+}
 
 __device__ __forceinline__ int resp_valid(const Problem& pr, int n) {
   if (pr.valid_len == nullptr) return pr.R;
@@ -75,24 +114,27 @@ static inline hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 g
 hipError_t launch_repack(const void* src, void* dst, int64_t row_bytes, int N, int P, int R,
                          int direction, hipStream_t stream);
 
-hipError_t launch_fwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
-                             const void* v, void* o, float* lse, hipStream_t stream);
-hipError_t launch_bwd_scalar(const Problem& pr, int dtype, const void* q, const void* k,
-                             const void* v, const void* o, const float* lse, const void* dout,
-                             void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+// `pr` carries the launch-wide fields (heads, dims, window, scale, Tld,
+// valid lengths); `G` the groups.
+hipError_t launch_fwd_scalar(const Problem& pr, const Groups& G, int dtype, const void* q,
+                             const void* k, const void* v, void* o, float* lse, hipStream_t stream);
+hipError_t launch_bwd_scalar(const Problem& pr, const Groups& G, int dtype, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* delta,
+                             hipStream_t stream);
 
-bool fwd_mfma_supported(const Problem& pr);
-hipError_t launch_fwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
-                           void* o, float* lse, hipStream_t stream);
+bool fwd_mfma_supported(const Problem& pr, const Groups& G);
+hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, const void* k,
+                           const void* v, void* o, float* lse, hipStream_t stream);
 
-bool bwd_mfma_supported(const Problem& pr);
-size_t bwd_mfma_workspace_bytes(const Problem& pr);
-hipError_t launch_bwd_mfma(const Problem& pr, const void* q, const void* k, const void* v,
-                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, void* workspace, hipStream_t stream);
+bool bwd_mfma_supported(const Problem& pr, const Groups& G);
+size_t bwd_mfma_workspace_bytes(const Problem& pr, const Groups& G);
+hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, void* workspace, hipStream_t stream);
 
-// Shared by the scalar backward and the MFMA backward: delta[h][t] =
-// sum_d dO[t,h,d] * O[t,h,d] in fp32 (0 on rows with no visible key).
+// Scalar backward: delta[h][t] = sum_d dO[t,h,d] * O[t,h,d] in fp32 (0 on
+// rows with no visible key) for all pr.Tld rows.
 hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const void* dout,
                             const float* lse, float* delta, hipStream_t stream);
 

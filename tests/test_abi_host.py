@@ -100,3 +100,65 @@ def test_strerror():
     assert lib.dualkv_strerror(0) == b"success"
     assert lib.dualkv_strerror(3) == b"workspace too small"
     assert lib.dualkv_strerror(99) == b"unknown status"
+
+
+def group_array(*gs):
+    return (dk.Group * max(1, len(gs)))(*[dk.Group(*g) for g in gs]), len(gs)
+
+
+def fwd_groups_status(p, arr, n):
+    d = ctypes.c_void_p(0x1000)
+    return dk.load_library().dualkv_fwd_groups(ctypes.byref(p), arr, n, d, d, d, d, d, None)
+
+
+def test_group_argument_checks():
+    lib = dk.load_library()
+    p = params()
+    arr, _ = group_array((2, 16, 8))
+    assert fwd_groups_status(p, arr, 0) == 1                           # no group
+    assert lib.dualkv_fwd_groups(ctypes.byref(p), None, 1, *[None] * 6) == 1
+    many, n = group_array(*[(1, 4, 4)] * (dk.MAX_GROUPS + 1))
+    assert fwd_groups_status(p, many, n) == 2                          # above the maximum
+    ok, n = group_array(*[(1, 4, 4)] * dk.MAX_GROUPS)
+    assert lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), ok, n) > 0
+    for bad in ((0, 4, 4), (1, -1, 4), (1, 4, -1)):
+        arr, n = group_array((2, 16, 8), bad)
+        assert fwd_groups_status(p, arr, n) == 1, bad
+        assert lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), arr, n) == 0
+    arr, n = group_array((3, 0, 0), (1, 0, 0))                         # no rows at all
+    assert lib.dualkv_fwd_groups(ctypes.byref(p), arr, n, *[None] * 6) == 0
+    d = ctypes.c_void_p(0x1000)
+    assert lib.dualkv_repack_groups(d, d, 16, None, 1, 0, None) == 1
+    assert lib.dualkv_repack_groups(d, d, 16, many, dk.MAX_GROUPS + 1, 0, None) == 2
+    arr, n = group_array((2, 3, 4), (0, 3, 4))
+    assert lib.dualkv_repack_groups(d, d, 16, arr, n, 0, None) == 1
+    arr, n = group_array((2, 0, 0), (1, 0, 0))
+    assert lib.dualkv_repack_groups(None, None, 16, arr, n, 1, None) == 0
+
+
+@pytest.mark.parametrize("dtype,impl", [(dk.DUALKV_BF16, dk.IMPL_AUTO), (dk.DUALKV_F32, dk.IMPL_AUTO),
+                                        (dk.DUALKV_BF16, dk.IMPL_SCALAR)])
+def test_one_group_matches_single_entry_points(dtype, impl):
+    lib = dk.load_library()
+    for N, P, R, W in ((4, 64, 32, 0), (8, 300, 70, 0), (3, 1000, 100, 128), (2, 0, 50, 0)):
+        p = params(n_resp=N, prompt_len=P, resp_len=R, window=W, dtype=dtype, impl=impl)
+        arr, n = group_array((N, P, R))
+        q = params(n_resp=99, prompt_len=7, resp_len=5, window=W, dtype=dtype, impl=impl)  # ignored fields
+        assert lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(q), arr, n) == \
+            lib.dualkv_bwd_workspace_bytes(ctypes.byref(p))
+
+
+def test_group_workspace_covers_every_row():
+    # per-row statistics for all rows of the launch, plus each group's partials
+    lib = dk.load_library()
+    p = params()
+    g1, g2 = (4, 640, 160), (8, 320, 64)
+    rows = sum(P + N * R for N, P, R in (g1, g2))
+    arr, n = group_array(g1, g2)
+    both = lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), arr, n)
+    assert both >= 2 * 4 * p.n_q_heads * rows
+    sep = 0
+    for g in (g1, g2):
+        a1, _ = group_array(g)
+        sep += lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), a1, 1)
+    assert both <= sep + 1024

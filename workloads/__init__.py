@@ -134,3 +134,69 @@ def generate(w: Workload, with_grad: bool = True) -> Inputs:
 
 def softmax_scale(w: Workload) -> float:
     return 1.0 / float(np.sqrt(w.head_dim))
+
+
+# ------------------------------------------------------------------ groups
+# A micro-batch that mixes prompts: groups g = 0.. of (N_g, P_g, R_g) laid
+# out one after the other in the packed rows (each group packed as above).
+
+@dataclasses.dataclass(frozen=True)
+class GroupedWorkload:
+    name: str
+    dtype: str
+    groups: tuple          # ((N, P, R), ...)
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int = 0
+    seed: int = 0
+    value_scale: float = 0.5
+    len_ranges: Optional[tuple] = None  # per group inclusive (lo, hi), or None (all R_g)
+    description: str = ""
+
+    @property
+    def packed_len(self) -> int:
+        return sum(P + N * R for N, P, R in self.groups)
+
+    @property
+    def replicated_len(self) -> int:
+        return sum(N * (P + R) for N, P, R in self.groups)
+
+    def replace(self, **kw) -> "GroupedWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+GROUPED = {
+    # three prompts of different lengths and group sizes in one Qwen3-8B-
+    # shaped micro-batch, ragged response lengths (38,912 packed tokens)
+    "qwen3_8b_groups": GroupedWorkload(
+        "qwen3_8b_groups", "bf16", ((8, 8192, 1024), (8, 4096, 1024), (16, 2048, 512)), 32, 8, 128,
+        seed=5, len_ranges=((256, 1024), (512, 1024), (128, 512)),
+        description="Qwen3-8B-shaped layer over three prompt groups, ragged responses"),
+}
+
+
+def generate_groups(w: GroupedWorkload, with_grad: bool = True) -> Inputs:
+    """Seeded inputs of a grouped workload, drawn like ``generate``: the
+    valid lengths of every group in group order (only if ``len_ranges``),
+    then Q, K, V, dO over all packed rows."""
+    rng = np.random.default_rng(w.seed)
+    valid = None
+    if w.len_ranges is not None:
+        valid = np.concatenate([rng.integers(lo, hi, endpoint=True, size=N)
+                                for (N, _, _), (lo, hi) in zip(w.groups, w.len_ranges)]).astype(np.int32)
+    T = w.packed_len
+
+    def draw(h):
+        a = rng.standard_normal((T, h, w.head_dim), dtype=np.float32)
+        if w.value_scale != 1.0:
+            a *= np.float32(w.value_scale)
+        if w.dtype == "bf16":
+            a = round_to_bf16(a)
+        return a
+
+    q = draw(w.n_q_heads)
+    k = draw(w.n_kv_heads)
+    v = draw(w.n_kv_heads)
+    do = draw(w.n_q_heads) if with_grad else None
+    return Inputs(q, k, v, do, valid)
