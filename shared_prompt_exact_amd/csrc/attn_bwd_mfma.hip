@@ -255,17 +255,20 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     };
-    static_assert(NS == 2 || NS == 3, "ring depth");
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
     if constexpr (D <= 128) {
       // unrolled by the ring depth (small head dims: registers to spare)
       int it = 0;
       for (; it + NS <= ntiles; it += NS) {
         step(it, IntC<0>{});
         step(it + 1, IntC<1>{});
-        if constexpr (NS == 3) step(it + 2, IntC<2>{});
+        if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
+        if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
       }
       if (it < ntiles) step(it, IntC<0>{});
-      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+      if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
+      if constexpr (NS == 4)
+        if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
     } else {
       for (int it = 0; it < ntiles; ++it) step(it, it % NS);
     }
@@ -741,7 +744,10 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
           const f32x16& ak = dKt[db][kt];
           const f32x16& av = dVt[db][kt];
           if (partial) {
-            const int64_t o = (((int64_t)it.slot * pr.P + it.k0 + my_k[kt]) * pr.Hkv + c) * D + d;
+            // partials cover prompt rows t0*BK .. P-1 only: [slots, P - t0*BK, Hkv, D]
+            const int prow0 = sh.t0 * C::BK;
+            const int64_t o =
+                (((int64_t)it.slot * (pr.P - prow0) + it.k0 + my_k[kt] - prow0) * pr.Hkv + c) * D + d;
             *reinterpret_cast<float4*>(part_k + o) =
                 make_float4(ak[4 * g4] * pr.scale, ak[4 * g4 + 1] * pr.scale, ak[4 * g4 + 2] * pr.scale,
                             ak[4 * g4 + 3] * pr.scale);
@@ -806,13 +812,13 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------ slot reduction
 
-// Per prompt group (blockIdx.y): prompt rows whose key tiles wrote
-// per-slot fp32 partials, float4 index i0 .. i0+n4-1 of the group's
-// [P, Hkv, D] prompt block (from float4 part4 of the partial buffers, slot
-// stride `stride4`); the sums go to dK/dV from 4-element index out4.
+// Per prompt group (blockIdx.y): the prompt rows whose key tiles wrote
+// per-slot fp32 partials, n4 float4s per slot from float4 part4 of the
+// partial buffers (slot stride `stride4`); the sums, cast, go to dK/dV
+// from 4-element index out4.
 struct RedGroups {
   int slots[kMaxGroups];
-  int64_t part4[kMaxGroups], stride4[kMaxGroups], i0[kMaxGroups], n4[kMaxGroups], out4[kMaxGroups];
+  int64_t part4[kMaxGroups], stride4[kMaxGroups], n4[kMaxGroups], out4[kMaxGroups];
 };
 
 __global__ void __launch_bounds__(256)
@@ -820,14 +826,13 @@ __global__ void __launch_bounds__(256)
                         uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   const int gi = blockIdx.y;
   const int slots = RG.slots[gi];
-  const int64_t stride4 = RG.stride4[gi], i0 = RG.i0[gi], n4 = RG.n4[gi];
+  const int64_t stride4 = RG.stride4[gi], n4 = RG.n4[gi];
   part_k += 4 * RG.part4[gi];
   part_v += 4 * RG.part4[gi];
   dk += 4 * RG.out4[gi];
   dv += 4 * RG.out4[gi];
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n4;
-       j += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t i = i0 + j;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
     float4 a = reinterpret_cast<const float4*>(part_k)[i];
     float4 b = reinterpret_cast<const float4*>(part_v)[i];
     for (int s = 1; s < slots; ++s) {     // ascending slot order
@@ -882,13 +887,18 @@ KvShape kv_shape(int N, int P, int R, int W, int BK) {
   KvShape sh;
   sh.nPt = (P + BK - 1) / BK;
   sh.nRt = (R + BK - 1) / BK;
-  // Slots of a prompt key tile: slot 0 holds the prompt's own queries (at
-  // most P of them); the responses are cut into ranges of about P queries
-  // each, so no slot is much longer than the longest prompt slot.
+  // Slots of a prompt key tile: slot 0 holds the prompt's own queries;
+  // the responses are cut into ranges of about as many queries as slot 0
+  // has, so no slot is much longer than the longest prompt slot.  Without
+  // a window slot 0 holds up to P queries and a response R of them; with a
+  // window W a prompt key is seen by at most W + BK - 1 prompt queries of
+  // its tile and by the first W queries of each response.
   int rslots = 0;
   if (P > 0 && R > 0) {
-    const int64_t nr = (int64_t)N * R;
-    rslots = (int)((nr + P - 1) / P);
+    const int64_t q_prompt = W > 0 ? std::min<int64_t>(P, (int64_t)W + BK) : P;
+    const int64_t q_resp = W > 0 ? std::min<int64_t>(R, W) : R;
+    const int64_t nr = (int64_t)N * q_resp;
+    rslots = (int)((nr + q_prompt - 1) / q_prompt);
     rslots = max(1, min(rslots, N));
   }
   sh.per_slot = rslots > 0 ? (N + rslots - 1) / rslots : 1;
@@ -923,23 +933,22 @@ BwdPlan plan(const Problem& pr, const Groups& G) {
     p.kg.sh[i] = sh;
     p.kg.off[i] = (int)std::min(items, kBig);
     items += (int64_t)(sh.nPt - sh.t0) * (sh.slots - 1) + sh.nPt + (int64_t)N * sh.nRt;
-    // fp32 partials [slots, P, Hkv, D] of this group, 256-byte aligned
+    // fp32 partials [slots, P - t0*BK, Hkv, D] of this group (the prompt
+    // rows whose key tiles have response slots), 256-byte aligned
     p.kg.part[i] = part;
     const int64_t row4 = (int64_t)pr.Hkv * pr.D / 4;   // float4s per prompt row
+    const int64_t r0 = std::min<int64_t>((int64_t)sh.t0 * BK, P);
     p.rg.slots[i] = sh.slots;
     p.rg.part4[i] = part / 4;
-    p.rg.stride4[i] = (int64_t)P * row4;
-    p.rg.out4[i] = (int64_t)G.row0[i] * row4;
+    p.rg.stride4[i] = (P - r0) * row4;
+    p.rg.out4[i] = ((int64_t)G.row0[i] + r0) * row4;
     if (sh.slots > 1 && sh.t0 < sh.nPt) {
-      // prompt rows t0*BK .. P-1: the rows whose tiles wrote slot partials
-      const int64_t r0 = (int64_t)sh.t0 * BK;
-      p.rg.i0[i] = r0 * row4;
       p.rg.n4[i] = (P - r0) * row4;
       p.reduce = true;
       red = std::max(red, p.rg.n4[i]);
-      part += (int64_t)align256((size_t)sh.slots * P * pr.Hkv * pr.D * sizeof(float)) / 4;
+      part += (int64_t)align256((size_t)sh.slots * (P - r0) * pr.Hkv * pr.D * sizeof(float)) / 4;
     } else {
-      p.rg.i0[i] = p.rg.n4[i] = 0;
+      p.rg.n4[i] = 0;
     }
   }
   p.gb.off[G.n] = (int)std::min(nb, kBig);

@@ -271,17 +271,20 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     };
-    static_assert(NS == 2 || NS == 3, "ring depth");
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
     if constexpr (D <= 128) {
       // unrolled by the ring depth (small head dims: registers to spare)
       int it = 0;
       for (; it + NS <= ntiles; it += NS) {
         step(it, IntC<0>{});
         step(it + 1, IntC<1>{});
-        if constexpr (NS == 3) step(it + 2, IntC<2>{});
+        if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
+        if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
       }
       if (it < ntiles) step(it, IntC<0>{});
-      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+      if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
+      if constexpr (NS == 4)
+        if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
     } else {
       for (int it = 0; it < ntiles; ++it) step(it, it % NS);
     }
