@@ -185,6 +185,113 @@ int dualkv_repack_groups(const void* src, void* dst, int64_t row_bytes,
                          const dualkv_group* groups, int32_t n_groups,
                          int32_t direction, void* stream);
 
+/* ------------------------------------------------------------------------
+ * A packed transformer layer (arXiv 2605.15422, Abstract: the packed layout
+ * reduces the tokens of the whole model, so every token-wise step runs on
+ * P+NR rows).  All tensors bf16, row-major, 16-byte aligned; fp32
+ * arithmetic inside every kernel.  Each entry point validates on the host
+ * and launches nothing on error.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * C[M][N] = A B (+ R), fp32 accumulation, bf16 result.  A is stored [M][K]
+ * (lda >= K), or with trans_a as [K][M] (lda >= M); B is [K][N] (ldb >= N),
+ * or with trans_b as [N][K] (ldb >= K); C and R are [M][N] (ldc, ldr >= N);
+ * R may be NULL or equal to C.  trans_a and trans_b are not both set.
+ * DUALKV_ERR_UNSUPPORTED for shapes the 128x128x64 tiles do not take: with
+ * trans_a M % 128 == 0; without trans_b N % 128 == 0; K % 64 == 0 unless
+ * trans_a is set and trans_b is not (K free there); lda, ldb multiples
+ * of 8.
+ */
+int dualkv_gemm_bf16(int32_t trans_a, int32_t trans_b, int32_t M, int32_t N,
+                     int32_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, const void* R,
+                     int64_t ldr, void* stream);
+
+/*
+ * RMSNorm of T rows of H (H % 8 == 0): rstd[t] = 1/sqrt(mean_i x[t][i]^2 +
+ * eps) (fp32 [T]), y = x * rstd * w.  The backward writes
+ * dx = rstd * (w*dy - xh * mean_i(w*dy*xh)) + dres (xh = x*rstd; dres may be
+ * NULL) and dw[i] = sum_t dy[t][i] * xh[t][i] (rows summed in a fixed
+ * order), using a workspace of dualkv_rmsnorm_bwd_workspace_bytes(T, H).
+ */
+int dualkv_rmsnorm_fwd(int32_t T, int32_t H, float eps, const void* x,
+                       const void* w, void* y, float* rstd, void* stream);
+size_t dualkv_rmsnorm_bwd_workspace_bytes(int32_t T, int32_t H);
+int dualkv_rmsnorm_bwd(int32_t T, int32_t H, const void* x, const void* w,
+                       const float* rstd, const void* dy, const void* dres,
+                       void* dx, void* dw, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Rotary position embedding, in place, on x [rows][n_heads][head_dim] of
+ * the packed groups: row t of a group has logical position t (prompt) or
+ * P + r (response row r), and the pair (i, i + head_dim/2) of every head is
+ * rotated by the angle pos * base^(-2i/head_dim) (by its negative with
+ * inverse = 1, which undoes the rotation).
+ */
+int dualkv_rope(const dualkv_group* groups, int32_t n_groups, int32_t n_heads,
+                int32_t head_dim, float base, int32_t inverse, void* x,
+                void* stream);
+
+/* SwiGLU over n elements (n % 8 == 0): m = silu(u) * g; backward
+ * du = dm * g * silu'(u), dg = dm * silu(u). */
+int dualkv_swiglu_fwd(int64_t n, const void* u, const void* g, void* m,
+                      void* stream);
+int dualkv_swiglu_bwd(int64_t n, const void* u, const void* g, const void* dm,
+                      void* du, void* dg, void* stream);
+
+/*
+ * Pre-norm decoder layer on the packed groups (Tld rows of `hidden`):
+ *   h1 = RMSNorm(x; norm1); q, k, v = h1 wq, h1 wk, h1 wv;
+ *   q, k = RoPE at the rows' logical positions;
+ *   o = shared-prompt attention (dualkv_fwd_groups, window, valid lengths);
+ *   x1 = x + o wo; h2 = RMSNorm(x1; norm2); m = silu(h2 w1) * (h2 w3);
+ *   y = x1 + m w2.
+ * Weights are [in][out]: wq [hidden][Hq*D], wk, wv [hidden][Hkv*D],
+ * wo [Hq*D][hidden], w1, w3 [hidden][ffn], w2 [ffn][hidden], norms [hidden].
+ * hidden, ffn, Hq*D and Hkv*D must be multiples of 128
+ * (DUALKV_ERR_UNSUPPORTED otherwise).  The forward keeps its activations in
+ * `saved` (dualkv_layer_saved_bytes, 256-byte aligned) for the backward,
+ * which writes dx and the weight gradients `grads` (same shapes as the
+ * weights, overwritten) using `workspace` (dualkv_layer_workspace_bytes,
+ * 256-byte aligned).  Each prompt's rows appear once, so the weight
+ * gradients sum each prompt token once, with the gradient it receives from
+ * all responses of its group.
+ */
+typedef struct dualkv_layer_params {
+  int32_t hidden;
+  int32_t n_q_heads, n_kv_heads, head_dim;
+  int32_t ffn;
+  int32_t window;                 /* attention window, <= 0: none */
+  float rope_base;                /* > 1 */
+  float norm_eps;                 /* > 0 */
+  const int32_t* resp_valid_len;  /* device int32 [sum N_i] or NULL */
+} dualkv_layer_params;
+
+typedef struct dualkv_layer_weights {
+  const void *norm1, *wq, *wk, *wv, *wo, *norm2, *w1, *w3, *w2;
+} dualkv_layer_weights;
+
+typedef struct dualkv_layer_grads {
+  void *norm1, *wq, *wk, *wv, *wo, *norm2, *w1, *w3, *w2;
+} dualkv_layer_grads;
+
+size_t dualkv_layer_saved_bytes(const dualkv_layer_params* p,
+                                const dualkv_group* groups, int32_t n_groups);
+size_t dualkv_layer_workspace_bytes(const dualkv_layer_params* p,
+                                    const dualkv_group* groups,
+                                    int32_t n_groups);
+int dualkv_layer_fwd(const dualkv_layer_params* p, const dualkv_group* groups,
+                     int32_t n_groups, const dualkv_layer_weights* w,
+                     const void* x, void* y, void* saved, size_t saved_bytes,
+                     void* stream);
+int dualkv_layer_bwd(const dualkv_layer_params* p, const dualkv_group* groups,
+                     int32_t n_groups, const dualkv_layer_weights* w,
+                     const void* x, const void* saved, size_t saved_bytes,
+                     const void* dy, void* dx, const dualkv_layer_grads* grads,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* dualkv_strerror(int status);
 

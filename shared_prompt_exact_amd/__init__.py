@@ -49,6 +49,22 @@ class Group(ctypes.Structure):
 
 MAX_GROUPS = 32
 
+LAYER_WEIGHTS = ("norm1", "wq", "wk", "wv", "wo", "norm2", "w1", "w3", "w2")
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("resp_valid_len", ctypes.c_void_p)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHTS]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHTS]
+
 
 def load_library():
     """Load libdualkv.so (once).  Raises if it has not been built."""
@@ -78,6 +94,23 @@ def load_library():
     lib.dualkv_bwd_groups_workspace_bytes.restype = sz
     lib.dualkv_bwd_groups.argtypes = [pp, gp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dualkv_bwd_groups.restype = ctypes.c_int
+    f32, i64p = ctypes.c_float, ctypes.c_int64
+    lib.dualkv_gemm_bf16.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.dualkv_rmsnorm_fwd.argtypes = [i32, i32, f32, vp, vp, vp, vp, vp]
+    lib.dualkv_rmsnorm_bwd_workspace_bytes.argtypes = [i32, i32]
+    lib.dualkv_rmsnorm_bwd_workspace_bytes.restype = sz
+    lib.dualkv_rmsnorm_bwd.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dualkv_rope.argtypes = [gp, i32, i32, i32, f32, i32, vp, vp]
+    lib.dualkv_swiglu_fwd.argtypes = [i64p, vp, vp, vp, vp]
+    lib.dualkv_swiglu_bwd.argtypes = [i64p, vp, vp, vp, vp, vp, vp]
+    lpp = ctypes.POINTER(LayerParams)
+    lib.dualkv_layer_saved_bytes.argtypes = [lpp, gp, i32]
+    lib.dualkv_layer_saved_bytes.restype = sz
+    lib.dualkv_layer_workspace_bytes.argtypes = [lpp, gp, i32]
+    lib.dualkv_layer_workspace_bytes.restype = sz
+    lib.dualkv_layer_fwd.argtypes = [lpp, gp, i32, ctypes.POINTER(LayerWeights), vp, vp, vp, sz, vp]
+    lib.dualkv_layer_bwd.argtypes = [lpp, gp, i32, ctypes.POINTER(LayerWeights), vp, vp, sz, vp, vp,
+                                     ctypes.POINTER(LayerGrads), vp, sz, vp]
     lib.dualkv_strerror.argtypes = [ctypes.c_int]
     lib.dualkv_strerror.restype = ctypes.c_char_p
     lib.dualkv_profile_start.argtypes = []
@@ -313,3 +346,140 @@ def dualkv_bwd_groups(q, k, v, o, lse, dout, groups, window=0, softmax_scale=0.0
                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                                  _stream()), "dualkv_bwd_groups")
     return dq, dk, dv
+
+
+# ------------------------------------------------------- packed layer ops
+# bf16 tensors throughout (include/dualkv.h, "A packed transformer layer").
+
+def dualkv_gemm_bf16(a, b, trans_a=False, trans_b=False, residual=None, out=None):
+    """C = op(a) op(b) (+ residual) for 2-D bf16 tensors; op transposes the
+    stored matrix when its flag is set."""
+    lib = load_library()
+    for t, n in ((a, "a"), (b, "b")):
+        _require(t, n, dtype=torch.bfloat16)
+        if t.dim() != 2:
+            raise ValueError(f"{n} must be 2-D")
+    M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
+    Kb, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    if K != Kb:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+    _require(out, "out", dtype=torch.bfloat16, shape=(M, N))
+    if residual is not None:
+        _require(residual, "residual", dtype=torch.bfloat16, shape=(M, N))
+    _check(lib.dualkv_gemm_bf16(int(trans_a), int(trans_b), M, N, K, _ptr(a), a.shape[1], _ptr(b), b.shape[1],
+                                _ptr(out), N, _ptr(residual), N, _stream()), "dualkv_gemm_bf16")
+    return out
+
+
+def dualkv_rmsnorm_fwd(x, w, eps=1e-6):
+    """(y, rstd) of RMSNorm over the last dimension of a 2-D bf16 x."""
+    lib = load_library()
+    _require(x, "x", dtype=torch.bfloat16)
+    T, H = x.shape
+    _require(w, "w", dtype=torch.bfloat16, shape=(H,))
+    y = torch.empty_like(x)
+    rstd = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _check(lib.dualkv_rmsnorm_fwd(T, H, eps, _ptr(x), _ptr(w), _ptr(y), _ptr(rstd), _stream()),
+           "dualkv_rmsnorm_fwd")
+    return y, rstd
+
+
+def dualkv_rmsnorm_bwd(x, w, rstd, dy, dres=None):
+    """(dx, dw) of RMSNorm; dres (optional) is added to dx."""
+    lib = load_library()
+    T, H = x.shape
+    for t, n in ((x, "x"), (dy, "dy")):
+        _require(t, n, dtype=torch.bfloat16, shape=(T, H))
+    _require(w, "w", dtype=torch.bfloat16, shape=(H,))
+    _require(rstd, "rstd", dtype=torch.float32, shape=(T,))
+    if dres is not None:
+        _require(dres, "dres", dtype=torch.bfloat16, shape=(T, H))
+    ws = torch.empty(max(256, int(lib.dualkv_rmsnorm_bwd_workspace_bytes(T, H))), dtype=torch.uint8,
+                     device=x.device)
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    _check(lib.dualkv_rmsnorm_bwd(T, H, _ptr(x), _ptr(w), _ptr(rstd), _ptr(dy), _ptr(dres), _ptr(dx), _ptr(dw),
+                                  _ptr(ws), ws.numel(), _stream()), "dualkv_rmsnorm_bwd")
+    return dx, dw
+
+
+def dualkv_rope(x, groups, base=1e4, inverse=False):
+    """Rotary embedding in place on x [rows, heads, head_dim] (bf16) of the
+    packed groups, at logical positions."""
+    lib = load_library()
+    _require(x, "x", dtype=torch.bfloat16)
+    arr, n, gs = _group_array(groups)
+    if x.dim() != 3 or x.shape[0] != packed_rows(gs):
+        raise ValueError(f"x {tuple(x.shape)} does not match the groups' {packed_rows(gs)} rows")
+    _check(lib.dualkv_rope(arr, n, x.shape[1], x.shape[2], base, int(inverse), _ptr(x), _stream()), "dualkv_rope")
+    return x
+
+
+def dualkv_swiglu_fwd(u, g):
+    lib = load_library()
+    _require(u, "u", dtype=torch.bfloat16)
+    _require(g, "g", dtype=torch.bfloat16, shape=u.shape)
+    m = torch.empty_like(u)
+    _check(lib.dualkv_swiglu_fwd(u.numel(), _ptr(u), _ptr(g), _ptr(m), _stream()), "dualkv_swiglu_fwd")
+    return m
+
+
+def dualkv_swiglu_bwd(u, g, dm):
+    lib = load_library()
+    for t, n in ((u, "u"), (g, "g"), (dm, "dm")):
+        _require(t, n, dtype=torch.bfloat16, shape=u.shape)
+    du, dg = torch.empty_like(u), torch.empty_like(u)
+    _check(lib.dualkv_swiglu_bwd(u.numel(), _ptr(u), _ptr(g), _ptr(dm), _ptr(du), _ptr(dg), _stream()),
+           "dualkv_swiglu_bwd")
+    return du, dg
+
+
+def make_layer_params(hidden, n_q_heads, n_kv_heads, head_dim, ffn, window=0, rope_base=1e4, norm_eps=1e-6,
+                      valid_len=None):
+    return LayerParams(hidden, n_q_heads, n_kv_heads, head_dim, ffn, window, rope_base, norm_eps,
+                       None if valid_len is None else valid_len.data_ptr())
+
+
+def _layer_weights(W, cls=LayerWeights):
+    return cls(*[W[n].data_ptr() for n in LAYER_WEIGHTS])
+
+
+def dualkv_layer_saved_bytes(p, groups):
+    arr, n, _ = _group_array(groups)
+    return int(load_library().dualkv_layer_saved_bytes(ctypes.byref(p), arr, n))
+
+
+def dualkv_layer_workspace_bytes(p, groups):
+    arr, n, _ = _group_array(groups)
+    return int(load_library().dualkv_layer_workspace_bytes(ctypes.byref(p), arr, n))
+
+
+def dualkv_layer_fwd(x, W, groups, p, saved=None, out=None):
+    """Forward of the packed layer: returns (y, saved)."""
+    lib = load_library()
+    arr, n, gs = _group_array(groups)
+    _require(x, "x", dtype=torch.bfloat16, shape=(packed_rows(gs), p.hidden))
+    need = int(lib.dualkv_layer_saved_bytes(ctypes.byref(p), arr, n))
+    saved = torch.empty(max(256, need), dtype=torch.uint8, device=x.device) if saved is None else saved
+    out = torch.empty_like(x) if out is None else out
+    w = _layer_weights(W)
+    _check(lib.dualkv_layer_fwd(ctypes.byref(p), arr, n, ctypes.byref(w), _ptr(x), _ptr(out), _ptr(saved),
+                                saved.numel(), _stream()), "dualkv_layer_fwd")
+    return out, saved
+
+
+def dualkv_layer_bwd(x, saved, dy, W, groups, p, workspace=None, dx=None, grads=None):
+    """Backward of the packed layer: returns (dx, {weight name: gradient})."""
+    lib = load_library()
+    arr, n, gs = _group_array(groups)
+    _require(dy, "dy", dtype=torch.bfloat16, shape=x.shape)
+    need = int(lib.dualkv_layer_workspace_bytes(ctypes.byref(p), arr, n))
+    if workspace is None:
+        workspace = torch.empty(max(256, need), dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x) if dx is None else dx
+    grads = {k: torch.empty_like(W[k]) for k in LAYER_WEIGHTS} if grads is None else grads
+    w, g = _layer_weights(W), _layer_weights(grads, LayerGrads)
+    _check(lib.dualkv_layer_bwd(ctypes.byref(p), arr, n, ctypes.byref(w), _ptr(x), _ptr(saved), saved.numel(),
+                                _ptr(dy), _ptr(dx), ctypes.byref(g), _ptr(workspace), workspace.numel(),
+                                _stream()), "dualkv_layer_bwd")
+    return dx, grads
