@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the CPU oracle sample")
+    ap.add_argument("--layer", action="store_true",
+                    help="time a whole packed decoder layer (projections, norms, RoPE, attention, MLP) "
+                         "instead of the attention step")
     return ap.parse_args()
 
 
@@ -98,6 +101,114 @@ def cpu_baseline(w, groups, x, seconds):
                        f"(prompt + response), {dt:.1f} s; rate counts useful pairs of the sample")}
 
 
+# Decoder-layer shapes of the attention workloads (hidden size, MLP width,
+# RoPE base): Qwen3-8B and the 30B MoE's attention width with a dense MLP of
+# the same width as Qwen3-8B's.
+LAYER_SHAPES = {"qwen3_8b": (4096, 12288, 1e6), "dapo_long": (4096, 12288, 1e6), "moe_30b": (4096, 12288, 1e6),
+                "qwen3_8b_groups": (4096, 12288, 1e6)}
+
+
+def layer_bench(args, dk, workloads, workcount, torch, dev):
+    """One step = forward + backward of one packed decoder layer (x and dy
+    resident), against the same layer on the replicated rows."""
+    import numpy as np
+    if args.workload not in LAYER_SHAPES:
+        print(f"no layer shape for {args.workload}", file=sys.stderr)
+        sys.exit(2)
+    grouped = args.workload in workloads.GROUPED
+    w = workloads.GROUPED[args.workload] if grouped else workloads.WORKLOADS[args.workload]
+    groups = w.groups if grouped else ((w.n_resp, w.prompt_len, w.resp_len),)
+    Hm, F, base = LAYER_SHAPES[args.workload]
+    Hq, Hkv, D, Wn = w.n_q_heads, w.n_kv_heads, w.head_dim, w.window
+    T, T_rep = w.packed_len, w.replicated_len
+    rng = np.random.default_rng(w.seed)
+    L = []
+    if grouped and w.len_ranges is not None:
+        for (N, P, R), (lo, hi) in zip(groups, w.len_ranges):
+            L += rng.integers(lo, hi, endpoint=True, size=N).tolist()
+    elif not grouped and w.len_range is not None:
+        L = rng.integers(w.len_range[0], w.len_range[1], endpoint=True, size=w.n_resp).tolist()
+    else:
+        L = [R for N, P, R in groups for _ in range(N)]
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    shapes = {"norm1": (Hm,), "wq": (Hm, Hq * D), "wk": (Hm, Hkv * D), "wv": (Hm, Hkv * D), "wo": (Hq * D, Hm),
+              "norm2": (Hm,), "w1": (Hm, F), "w3": (Hm, F), "w2": (F, Hm)}
+    W = {}
+    for n, sh in shapes.items():
+        if n.startswith("norm"):
+            W[n] = (1 + 0.1 * torch.randn(sh, generator=g, device=dev)).to(torch.bfloat16)
+        else:
+            W[n] = (torch.randn(sh, generator=g, device=dev) / np.sqrt(sh[0])).to(torch.bfloat16)
+    x = torch.randn((T, Hm), generator=g, device=dev).to(torch.bfloat16)
+    dy = torch.randn((T, Hm), generator=g, device=dev).to(torch.bfloat16)
+    valid = torch.tensor(L, dtype=torch.int32, device=dev)
+
+    def setup(groups_, x_, dy_, valid_):
+        p = dk.make_layer_params(Hm, Hq, Hkv, D, F, Wn, base, 1e-6, valid_)
+        saved = torch.empty(dk.dualkv_layer_saved_bytes(p, groups_), dtype=torch.uint8, device=dev)
+        ws = torch.empty(dk.dualkv_layer_workspace_bytes(p, groups_), dtype=torch.uint8, device=dev)
+        y, dx = torch.empty_like(x_), torch.empty_like(x_)
+        grads = {n: torch.empty_like(W[n]) for n in W}
+
+        def step():
+            dk.dualkv_layer_fwd(x_, W, groups_, p, saved=saved, out=y)
+            dk.dualkv_layer_bwd(x_, saved, dy_, W, groups_, p, workspace=ws, dx=dx, grads=grads)
+        return step
+
+    print(f"[bench] layer {w.name}: packed {T} rows", file=sys.stderr, flush=True)
+    step = setup(groups, x, dy, valid)
+    for _ in range(args.warmup):
+        step()
+    ms = timed(step, args.steps, torch)
+    dk.dualkv_profile_start()
+    for _ in range(args.steps):
+        step()
+    prof = {k: round(v[1] / args.steps, 3) for k, v in dk.dualkv_profile_stop().items()}
+    torch.cuda.empty_cache()
+    rep = None
+    if not args.no_replicated:
+        print(f"[bench] layer {w.name}: replicated {T_rep} rows", file=sys.stderr, flush=True)
+        rgroups = tuple((N, 0, P + R) for N, P, R in groups)
+        xr = torch.empty((T_rep, Hm), dtype=torch.bfloat16, device=dev)
+        dyr = torch.empty_like(xr)
+        dk.dualkv_repack_groups(x, groups, dk.DUALKV_SCATTER, out=xr)
+        dk.dualkv_repack_groups(dy, groups, dk.DUALKV_SCATTER, out=dyr)
+        vr, i = [], 0
+        for N, P, R in groups:
+            vr += [P + l for l in L[i:i + N]]
+            i += N
+        rstep = setup(rgroups, xr, dyr, torch.tensor(vr, dtype=torch.int32, device=dev))
+        rstep()
+        rsteps = max(2, args.steps // 2)
+        rms = timed(rstep, rsteps, torch)
+        rep = {"ms_fwd_bwd": round(rms, 3), "speedup": round(rms / ms, 3)}
+        del rstep, xr, dyr
+        torch.cuda.empty_cache()
+    lin = Hm * (Hq * D + 2 * Hkv * D) + Hq * D * Hm + 3 * Hm * F
+    Li, pairs, rep_pairs = 0, 0, 0
+    for N, P, R in groups:
+        pairs += workcount.visible_pairs(N, P, R, Wn, L[Li:Li + N])
+        rep_pairs += workcount.replicated_pairs(N, P, R, Wn, L[Li:Li + N])
+        Li += N
+    gemm_fl = 6 * T * lin
+    att_fl = 14 * pairs * Hq * D
+    line = {"metric": "packed decoder layer fwd+bwd TFLOP/s (projections, norms, RoPE, attention, MLP)",
+            "value": round((gemm_fl + att_fl) / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (random weights and activations of the layer shape)",
+            "config": {"workload": w.name, "groups": [list(x_) for x_ in groups], "hidden": Hm, "ffn": F,
+                       "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "window": Wn,
+                       "packed_tokens": T, "replicated_tokens": T_rep},
+            "flops": {"gemm": gemm_fl, "attention": att_fl},
+            "rho": round(T_rep / T, 4),
+            # useful-FLOP ratio of the two layouts: token-wise work scales with
+            # the rows, attention with the visible pairs
+            "rho_layer": round((6 * T_rep * lin + 14 * rep_pairs * Hq * D) / (gemm_fl + att_fl), 4),
+            "replicated": rep, "kernels_ms_per_step": prof}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -115,6 +226,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.layer:
+        layer_bench(args, dk, workloads, workcount, torch, dev)
+        return
     grouped = args.workload in workloads.GROUPED
     if grouped:
         w = workloads.GROUPED[args.workload]

@@ -40,6 +40,14 @@ KERNELS = {
     "bwd_reduce": ("reduce_slots_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_delta": ("delta_lse2_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "repack": ("repack_kernel", ["repack.hip", "common.h"]),
+    "gemm": ("gemm_bf16_kernel", ["gemm.hip"] + _HEADERS),
+    "rmsnorm_fwd": ("rmsnorm_fwd_kernel", ["layer_ops.hip", "common.h"]),
+    "rmsnorm_bwd": ("rmsnorm_bwd_kernel", ["layer_ops.hip", "common.h"]),
+    "norm_wgrad": ("norm_wgrad_partial_kernel", ["layer_ops.hip", "common.h"]),
+    "norm_wgrad_sum": ("sum_chunks_kernel", ["layer_ops.hip", "common.h"]),
+    "rope": ("rope_kernel", ["layer_ops.hip", "common.h"]),
+    "swiglu_fwd": ("swiglu_fwd_kernel", ["layer_ops.hip", "common.h"]),
+    "swiglu_bwd": ("swiglu_bwd_kernel", ["layer_ops.hip", "common.h"]),
 }
 
 
@@ -83,11 +91,16 @@ def kernels_summary(stats_dir, bench_log, out_path, title, cmd):
         sym = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("dualkv::", "")
         out.append(f"| {short_name(r['Name'])} | `{sym}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                    f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
-    out += ["", "Same run, bench.py's own timing (HIP events): step %.3f ms, fwd %.3f ms, bwd %.3f ms." % (
-        b["ms_per_step"], b["fwd"]["ms"], b["bwd"]["ms"]),
-        "Per-kernel averages from the library's event profiler inside the timed steps: " +
-        ", ".join(f"{k} {v['avg_ms']:.3f} ms" for k, v in b["kernels"].items()) + ".", "",
-        "Dominant kernel roofline as bench.py reports it: `" + json.dumps(b["roofline"]) + "`", ""]
+    if "kernels_ms_per_step" in b:        # the decoder-layer line
+        out += ["", "Same run, bench.py's own timing (HIP events): step %.3f ms." % b["ms_per_step"],
+                "Per-step kernel time from the library's event profiler inside the timed steps: " +
+                ", ".join(f"{k} {v:.3f} ms" for k, v in b["kernels_ms_per_step"].items()) + ".", ""]
+    else:
+        out += ["", "Same run, bench.py's own timing (HIP events): step %.3f ms, fwd %.3f ms, bwd %.3f ms." % (
+            b["ms_per_step"], b["fwd"]["ms"], b["bwd"]["ms"]),
+            "Per-kernel averages from the library's event profiler inside the timed steps: " +
+            ", ".join(f"{k} {v['avg_ms']:.3f} ms" for k, v in b["kernels"].items()) + ".", "",
+            "Dominant kernel roofline as bench.py reports it: `" + json.dumps(b["roofline"]) + "`", ""]
     with open(out_path, "w") as fh:
         fh.write("\n".join(out))
     return "\n".join(out)
