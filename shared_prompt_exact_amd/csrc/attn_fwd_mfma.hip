@@ -262,12 +262,22 @@ __global__ void __launch_bounds__(NW * 64)
               l += p;
               pB[2 * kb + hs][j] = (__bf16)p;
             }
-#pragma unroll
-        for (int db = 0; db < DBH; ++db) {
+        if constexpr (DBH <= 4) {
+          // k-step outer: the DBH accumulators are independent, so
+          // consecutive MFMAs do not wait on each other
 #pragma unroll
           for (int ks = 0; ks < K16; ++ks)
-            acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
-          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < DBH; ++db)
+              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
+        } else {
+#pragma unroll
+          for (int db = 0; db < DBH; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < K16; ++ks)
+              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
+            if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     };
