@@ -177,11 +177,33 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
         if (kind != 0) {
+          if constexpr (KTH <= 8) {
+            // the two operand reads of k-step kk+1 are issued before the
+            // two MFMAs of step kk (scheduling fences keep them there), so
+            // their latency overlaps MFMA work
+            bf16x8 ka = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
+            bf16x8 va = row_operand<D>(Vs, kb * 32 + l32, dh * KTH, hf);
 #pragma unroll
-          for (int kk = 0; kk < KTH; ++kk) {
-            s = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s);
-            dp = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp);
-            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < KTH; ++kk) {
+              bf16x8 kn = ka, vn = va;
+              if (kk + 1 < KTH) {
+                kn = row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk + 1, hf);
+                vn = row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk + 1, hf);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              s = mfma32(ka, qB[kk], s);
+              dp = mfma32(va, doB[kk], dp);
+              __builtin_amdgcn_sched_barrier(0);
+              ka = kn;
+              va = vn;
+            }
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < KTH; ++kk) {
+              s = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s);
+              dp = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp);
+              if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
         if constexpr (DS > 1) {
@@ -598,18 +620,42 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kt][i] = dp[kt][i] = 0.f;
       if (kind != 0) {
+        if constexpr (KW == 1 && !VREG && KTH <= 8) {
+          // the operand reads of k-step kk+1 are issued before the two
+          // MFMAs of step kk (scheduling fences keep them there)
+          const int kc0 = dh * KTH;
+          bf16x8 qa = row_operand<D>(Qs, l32, kc0, hf), da = row_operand<D>(DOs, l32, kc0, hf);
+          bf16x8 vb = row_operand<D>(Vs, wk0 + l32, kc0, hf);
 #pragma unroll
-        for (int kk = 0; kk < KTH; ++kk) {
-          const int kc = dh * KTH + kk;
-          const bf16x8 qa = row_operand<D>(Qs, l32, kc, hf);
-          const bf16x8 da = row_operand<D>(DOs, l32, kc, hf);
-#pragma unroll
-          for (int kt = 0; kt < KW; ++kt) {
-            const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + 32 * kt + l32, kc, hf);
-            s[kt] = mfma32(qa, kB[kt][kk], s[kt]);
-            dp[kt] = mfma32(da, vb, dp[kt]);
+          for (int kk = 0; kk < KTH; ++kk) {
+            bf16x8 qn = qa, dn = da, vn = vb;
+            if (kk + 1 < KTH) {
+              qn = row_operand<D>(Qs, l32, kc0 + kk + 1, hf);
+              dn = row_operand<D>(DOs, l32, kc0 + kk + 1, hf);
+              vn = row_operand<D>(Vs, wk0 + l32, kc0 + kk + 1, hf);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            s[0] = mfma32(qa, kB[0][kk], s[0]);
+            dp[0] = mfma32(da, vb, dp[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            qa = qn;
+            da = dn;
+            vb = vn;
           }
-          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KTH; ++kk) {
+            const int kc = dh * KTH + kk;
+            const bf16x8 qa = row_operand<D>(Qs, l32, kc, hf);
+            const bf16x8 da = row_operand<D>(DOs, l32, kc, hf);
+#pragma unroll
+            for (int kt = 0; kt < KW; ++kt) {
+              const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + 32 * kt + l32, kc, hf);
+              s[kt] = mfma32(qa, kB[kt][kk], s[kt]);
+              dp[kt] = mfma32(da, vb, dp[kt]);
+            }
+            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       if constexpr (DS > 1) {
