@@ -8,10 +8,12 @@
 // B is stored [K][N] or, with TB, transposed as [N][K].  The three forms a
 // linear layer needs: y = x W (NN), dx = dy W^T (NT), dW = x^T dy (TN).
 //
-// Tiling: a workgroup of four waves computes a 128 x 128 block of C, each
-// wave 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16; K advances 64
-// at a time through a two-slot LDS ring filled by direct global->LDS
-// loads (the same swizzled tile layout as the attention kernels).  Both
+// Tiling: a workgroup computes a BM x 128 block of C (BM = 256 with eight
+// waves and a three-slot ring where the rows allow, else 128 with four
+// waves and two slots), each wave 64 x 64 as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16; K advances 64 at a time through an LDS ring
+// filled by direct global->LDS loads (the same swizzled tile layout as the
+// attention kernels).  Both
 // operands number their k-slots in the order of the attention kernels'
 // transposed reads (half h of a 16-step holds k = 8*(j/4) + 4*h + j%4), so
 // k-major tiles are read transposed and m- or n-major tiles with two
@@ -28,10 +30,22 @@
 namespace dualkv {
 namespace {
 
-constexpr int GBM = 128, GBN = 128, GBK = 64, GNS = 2;
-constexpr int G_TILE = GBM * GBK;            // elements per A (or B) tile
-constexpr int G_STAGE = 2 * G_TILE;          // A tile then B tile
-constexpr int G_LDS = GNS * G_STAGE * 2;     // bytes
+constexpr int GBN = 128, GBK = 64;
+
+// Tile of BM x 128 (BM = 128: four waves, a two-slot ring, two workgroups
+// per CU; BM = 256: eight waves, a three-slot ring, one workgroup per CU,
+// tile loads two k-steps ahead).
+template <int BM>
+struct GemmCfg {
+  static constexpr int NW = BM / 32;              // waves, each a 64 x 64 quadrant
+  static constexpr int NS = BM == 256 ? 3 : 2;    // ring slots
+  static constexpr int A_ELEMS = BM * GBK, B_ELEMS = GBN * GBK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDS = NS * STAGE * 2;      // bytes
+  static constexpr int ABLK = A_ELEMS * 2 / 1024, BBLK = B_ELEMS * 2 / 1024;   // 1-KiB blocks
+  static constexpr int APW = ABLK / NW, BPW = BBLK / NW;                        // per wave
+  static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile blocks split evenly over the waves");
+};
 
 // A/B operand from an m- (or n-) major tile [rows][64 k]: row `row`,
 // 16-step ks, wave half hf, k-slots in the transposed-read order.
@@ -45,32 +59,34 @@ __device__ __forceinline__ bf16x8 kslot_row_operand(const uint16_t* tile, int ro
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <bool TA, bool TB>
-__global__ void __launch_bounds__(256)
+template <bool TA, bool TB, int BM>
+__global__ void __launch_bounds__(BM * 2)
     gemm_bf16_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
                      const uint16_t* __restrict__ B, int64_t ldb, uint16_t* C, int64_t ldc,
                      const uint16_t* R, int64_t ldr, int tiles_n) {
+  using G = GemmCfg<BM>;
+  constexpr int NS = G::NS;
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;     // 64 x 64 quadrant of the wave
   const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
-  const int m0 = bm * GBM, n0 = bn * GBN;
+  const int m0 = bm * BM, n0 = bn * GBN;
   const int nk = (K + GBK - 1) / GBK;
 
-  // this wave's 4 of the 16 1-KiB blocks of each tile
+  // this wave's share of the 1-KiB blocks of each tile
   auto issue = [&](int t) {
-    uint16_t* As = lds + (t % GNS) * G_STAGE;
-    uint16_t* Bs = As + G_TILE;
+    uint16_t* As = lds + (t % NS) * G::STAGE;
+    uint16_t* Bs = As + G::A_ELEMS;
     const int k0 = t * GBK;
-    if constexpr (TA)   // [K][M]: 64 rows of k, 128 m each
-      dma_rows<GBM>(A + (int64_t)k0 * lda + m0, lda, min(GBK, K - k0), As, wave * 4, 4, lane);
-    else                // [M][K]: 128 rows of m, 64 k each
-      dma_rows<GBK>(A + (int64_t)m0 * lda + k0, lda, min(GBM, M - m0), As, wave * 4, 4, lane);
+    if constexpr (TA)   // [K][M]: 64 rows of k, BM m each
+      dma_rows<BM>(A + (int64_t)k0 * lda + m0, lda, min(GBK, K - k0), As, wave * G::APW, G::APW, lane);
+    else                // [M][K]: BM rows of m, 64 k each
+      dma_rows<GBK>(A + (int64_t)m0 * lda + k0, lda, min(BM, M - m0), As, wave * G::APW, G::APW, lane);
     if constexpr (TB)   // [N][K]
-      dma_rows<GBK>(B + (int64_t)n0 * ldb + k0, ldb, min(GBN, N - n0), Bs, wave * 4, 4, lane);
+      dma_rows<GBK>(B + (int64_t)n0 * ldb + k0, ldb, min(GBN, N - n0), Bs, wave * G::BPW, G::BPW, lane);
     else                // [K][N]
-      dma_rows<GBN>(B + (int64_t)k0 * ldb + n0, ldb, min(GBK, K - k0), Bs, wave * 4, 4, lane);
+      dma_rows<GBN>(B + (int64_t)k0 * ldb + n0, ldb, min(GBK, K - k0), Bs, wave * G::BPW, G::BPW, lane);
   };
 
   f32x16 acc[2][2];
@@ -81,21 +97,27 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  issue(0);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nk) issue(t);
   for (int t = 0; t < nk; ++t) {
-    wait_vmcnt<0>();                           // this wave's blocks of tile t
-    block_sync();                              // everyone's; slot (t+1)%2 is free
-    if (t + 1 < nk) issue(t + 1);
-    uint16_t* As = lds + (t % GNS) * G_STAGE;
-    uint16_t* Bs = As + G_TILE;
+    // tile t has landed once only the later tiles' loads (up to NS-2 of
+    // them, APW + BPW instructions each) are pending
+    if (NS == 3 && t + 1 < nk) wait_vmcnt<(NS - 2) * (G::APW + G::BPW)>();
+    else wait_vmcnt<0>();
+    block_sync();                              // everyone's; slot (t-1)%NS is free
+    if (t + NS - 1 < nk) issue(t + NS - 1);
+    uint16_t* As = lds + (t % NS) * G::STAGE;
+    uint16_t* Bs = As + G::A_ELEMS;
     if constexpr (TA && !TB) {
       const int kv = K - t * GBK;              // valid k rows of this tile
       if (kv < GBK) {
         // rows kv..63 of both k-major tiles re-read row kv-1: zero them
-        for (int r = kv + (tid >> 4); r < GBK; r += 16) {
-          const int c = tid & 15;              // 16 chunks of 8 elements per 128-wide row
-          *reinterpret_cast<uint4*>(As + r * GBM + c * 8) = uint4{0, 0, 0, 0};
-          *reinterpret_cast<uint4*>(Bs + r * GBN + c * 8) = uint4{0, 0, 0, 0};
+        constexpr int CA = BM / 8, CB = GBN / 8;   // 16-byte chunks per row
+        for (int i = tid; i < (GBK - kv) * (CA + CB); i += BM * 2) {
+          const int r = kv + i / (CA + CB), c = i % (CA + CB);
+          if (c < CA) *reinterpret_cast<uint4*>(As + r * BM + c * 8) = uint4{0, 0, 0, 0};
+          else *reinterpret_cast<uint4*>(Bs + r * GBN + (c - CA) * 8) = uint4{0, 0, 0, 0};
         }
         block_sync();
       }
@@ -106,7 +128,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int mr = wm * 64 + i * 32;
-        if constexpr (TA) a[i] = trans_operand<GBM>(As, 0, mr, ks, lane);
+        if constexpr (TA) a[i] = trans_operand<BM>(As, 0, mr, ks, lane);
         else a[i] = kslot_row_operand(As, mr + l32, ks, hf);
         const int nr = wn * 64 + i * 32;
         if constexpr (TB) b[i] = kslot_row_operand(Bs, nr + l32, ks, hf);
@@ -138,15 +160,24 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, int BM>
 hipError_t run_gemm(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                     int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
-  static const hipError_t attr = allow_lds(gemm_bf16_kernel<TA, TB>, G_LDS);
+  using G = GemmCfg<BM>;
+  static_assert(G::LDS <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = allow_lds(gemm_bf16_kernel<TA, TB, BM>, G::LDS);
   if (attr != hipSuccess) return attr;
-  const int tm = (M + GBM - 1) / GBM, tn = (N + GBN - 1) / GBN;
-  return launch("gemm", gemm_bf16_kernel<TA, TB>, dim3((unsigned)(tm * tn)), dim3(256), G_LDS, stream, M, N, K,
-                static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
+  const int tm = (M + BM - 1) / BM, tn = (N + GBN - 1) / GBN;
+  return launch("gemm", gemm_bf16_kernel<TA, TB, BM>, dim3((unsigned)(tm * tn)), dim3(BM * 2), G::LDS, stream, M,
+                N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
                 static_cast<uint16_t*>(C), ldc, static_cast<const uint16_t*>(R), ldr, tn);
+}
+
+// The 256-row tile where the rows allow it: whole 256-row blocks when A is
+// k-major; otherwise enough rows that 256-row blocks fill the chip.
+bool use_tall(bool ta, int M, int N) {
+  if (ta) return M % 256 == 0;
+  return (int64_t)((M + 255) / 256) * ((N + GBN - 1) / GBN) >= 512;
 }
 
 }  // namespace
@@ -158,12 +189,12 @@ int gemm_shape_ok(bool ta, bool tb, int M, int N, int K, int64_t lda, int64_t ld
   if (ldc < N) return 0;
   if (ta && tb) return 0;
   if (K == 0) return 1;                        // C = R (or 0): no operand is read
-  if (ta && M % GBM != 0) return 0;            // k-major A: whole 128-wide m blocks
+  if (ta && M % 128 != 0) return 0;            // k-major A: whole 128-wide m blocks
   if (!tb && N % GBN != 0) return 0;           // k-major B: whole 128-wide n blocks
   if (!(ta && !tb) && K % GBK != 0) return 0;  // k along tile columns: whole 64-wide k blocks
   // 16-byte global rows for the direct-to-LDS loads
   if (lda % 8 != 0 || ldb % 8 != 0) return 0;
-  if ((int64_t)((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN) >= ((int64_t)1 << 31)) return 0;
+  if ((int64_t)((M + 127) / 128) * ((N + GBN - 1) / GBN) >= ((int64_t)1 << 31)) return 0;
   return 1;
 }
 
@@ -171,9 +202,15 @@ hipError_t launch_gemm(bool ta, bool tb, int M, int N, int K, const void* A, int
                        int64_t ldb, void* C, int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (ta && tb) return hipErrorInvalidValue;
-  if (ta) return run_gemm<true, false>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
-  if (tb) return run_gemm<false, true>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
-  return run_gemm<false, false>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+  const bool tall = use_tall(ta, M, N);
+  if (ta)
+    return tall ? run_gemm<true, false, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+                : run_gemm<true, false, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+  if (tb)
+    return tall ? run_gemm<false, true, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+                : run_gemm<false, true, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+  return tall ? run_gemm<false, false, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+              : run_gemm<false, false, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
 }
 
 }  // namespace dualkv

@@ -1,7 +1,7 @@
 """The packed transformer layer and its token-wise kernels: HIP vs fp64 oracle.
 
- * GEMM (the three forms of a linear layer, ragged rows, a ragged k for the
-   weight-gradient form, a residual) against fp64 products of the same bf16
+ * GEMM (the three forms of a linear layer, both tile heights, ragged rows,
+   a ragged k for the weight-gradient form, a residual) against fp64 products of the same bf16
    inputs: the only differences are the fp32 accumulation order and the
    final bf16 rounding (at most 2^-9 relative), so rel-L2 <= 2e-3;
  * RMSNorm, RoPE at logical positions, SwiGLU, forward and backward,
@@ -47,6 +47,8 @@ def tight(name, got, want, rel=2e-3):
 @pytest.mark.parametrize("ta,tb,M,N,K,res", [
     (0, 0, 300, 256, 192, False), (0, 0, 1000, 512, 1024, True), (0, 1, 300, 384, 256, False),
     (1, 0, 256, 384, 200, False), (1, 0, 128, 128, 64, True), (1, 0, 384, 256, 1001, False),
+    # enough 256-row blocks for the eight-wave tile in the row-major forms
+    (0, 0, 4000, 4096, 256, True), (0, 1, 4000, 4096, 128, False),
 ])
 def test_gemm(ta, tb, M, N, K, res):
     print(f"gemm ta={ta} tb={tb} M={M} N={N} K={K} residual={res}", flush=True)
