@@ -334,6 +334,19 @@ def main():
                 "frac": round(dom_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": None if trec is None else trec["bytes_per_launch"]}
 
+    # The dense bf16 rate this device sustains (MFMA-only probe, no memory
+    # traffic), reported beside the published peak.
+    dk.dualkv_mfma_probe(1024, 50)
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record()
+    probe_fl = dk.dualkv_mfma_probe(1024, 2000)
+    e_ev.record()
+    torch.cuda.synchronize()
+    achievable = probe_fl / (s_ev.elapsed_time(e_ev) * 1e-3) / 1e12
+    roofline["achievable_peak"] = round(achievable, 1)
+    roofline["frac_of_achievable"] = round(dom_ach / achievable, 4)
+
     # Repack of hidden-state-sized rows (Hq*D bf16 per token), HBM bound.
     rep_rows = torch.empty((T_rep,) + tuple(do.shape[1:]), dtype=do.dtype, device=dev)
     repack(do, dk.DUALKV_SCATTER, rep_rows)
@@ -412,6 +425,10 @@ def main():
         "kernels": {k_: {kk: round(vv, 4) for kk, vv in d.items()} for k_, d in kernels.items()},
         "repack_hidden_rows": {"gather_GBs": round(gather_gbs, 1), "scatter_GBs": round(scatter_gbs, 1),
                                "row_bytes": row_b},
+        # Delta / scaled-LSE kernel: reads O, dO (bf16) and LSE, writes Delta
+        # and the scaled LSE (fp32): T*Hq*(4*D + 12) bytes
+        "bwd_delta_GBs": round(T * Hq * (4 * D + 12) / (kernels["bwd_delta"]["avg_ms"] * 1e-3) / 1e9, 1)
+        if "bwd_delta" in kernels else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

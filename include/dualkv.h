@@ -313,6 +313,16 @@ int dualkv_profile_stop(void);
 int dualkv_profile_count(void);
 int dualkv_profile_kernel(int index, const char** name, int64_t* launches, double* total_ms);
 
+/*
+ * Matrix-core rate probe for measurement tools: enqueues one kernel of
+ * `workgroups` x 512 threads in which every wave issues `iters` x 4
+ * independent bf16 32x32x16 MFMAs (no memory traffic) and returns the
+ * number of floating-point operations it performs (-1 on a bad argument
+ * or launch error).  Timing it with events on `stream` gives the dense
+ * bf16 rate the device sustains.  It writes no memory.
+ */
+int64_t dualkv_mfma_probe(int32_t workgroups, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

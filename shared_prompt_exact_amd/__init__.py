@@ -111,6 +111,8 @@ def load_library():
     lib.dualkv_layer_fwd.argtypes = [lpp, gp, i32, ctypes.POINTER(LayerWeights), vp, vp, vp, sz, vp]
     lib.dualkv_layer_bwd.argtypes = [lpp, gp, i32, ctypes.POINTER(LayerWeights), vp, vp, sz, vp, vp,
                                      ctypes.POINTER(LayerGrads), vp, sz, vp]
+    lib.dualkv_mfma_probe.argtypes = [i32, i32, vp]
+    lib.dualkv_mfma_probe.restype = ctypes.c_int64
     lib.dualkv_strerror.argtypes = [ctypes.c_int]
     lib.dualkv_strerror.restype = ctypes.c_char_p
     lib.dualkv_profile_start.argtypes = []
@@ -234,6 +236,14 @@ def dualkv_bwd(q, k, v, o, lse, dout, n_resp, prompt_len, resp_len, window=0, so
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()),
            "dualkv_bwd")
     return dq, dk, dv
+
+
+def dualkv_mfma_probe(workgroups, iters):
+    """Enqueue the matrix-core rate probe on the current stream; returns its FLOPs."""
+    fl = int(load_library().dualkv_mfma_probe(workgroups, iters, _stream()))
+    if fl < 0:
+        raise RuntimeError("dualkv_mfma_probe failed")
+    return fl
 
 
 def dualkv_profile_start():

@@ -117,3 +117,46 @@ int dualkv_profile_kernel(int index, const char** name, int64_t* launches, doubl
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ MFMA probe
+//
+// The matrix-core rate this device sustains: every wave issues back-to-back
+// v_mfma_f32_32x32x16_bf16 into four independent accumulators (no memory
+// traffic, no dependences between consecutive MFMAs).  Measurement tools
+// report it beside the published peak as the achievable ceiling.
+namespace {
+
+typedef __bf16 probe_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(512) mfma_probe_kernel(int iters, float* out) {
+  probe_bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)((threadIdx.x & 7) * 0.125f);
+    b[i] = (__bf16)(i * 0.0625f);
+  }
+  probe_f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  if (out) out[blockIdx.x] = s;   // the launch passes null: nothing is written, the loop stays
+}
+
+}  // namespace
+
+extern "C" int64_t dualkv_mfma_probe(int32_t workgroups, int32_t iters, void* stream) {
+  if (workgroups < 1 || iters < 1) return -1;
+  void* args[] = {&iters, nullptr};
+  float* out = nullptr;
+  args[1] = &out;
+  if (hipLaunchKernel(reinterpret_cast<const void*>(mfma_probe_kernel), dim3(workgroups), dim3(512), args, 0,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return -1;
+  // 8 waves x iters x 4 MFMAs x 32*32*16*2 flops per workgroup
+  return (int64_t)workgroups * 8 * iters * 4 * 32768;
+}
