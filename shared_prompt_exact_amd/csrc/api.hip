@@ -32,18 +32,36 @@ int validate_params(const dualkv_params* p, Problem* pr) {
   return DUALKV_OK;
 }
 
-// Validate the groups and fill `G` and the row counts of `pr` (N, P, R, T
-// of group 0; Tld of the whole launch).
-int validate_groups(const dualkv_group* groups, int32_t n, Problem* pr, Groups* G) {
+}  // namespace
+
+int dualkv::check_groups(const dualkv_group* groups, int32_t n, int64_t* rows) {
   if (groups == nullptr || n < 1) return DUALKV_ERR_INVALID_ARGUMENT;
   if (n > kMaxGroups) return DUALKV_ERR_UNSUPPORTED;
-  int64_t rows = 0, vl = 0;
-  G->n = n;
+  int64_t r = 0;
   for (int i = 0; i < n; ++i) {
     const dualkv_group& g = groups[i];
     if (g.n_resp < 1 || g.prompt_len < 0 || g.resp_len < 0) return DUALKV_ERR_INVALID_ARGUMENT;
     const int64_t T = (int64_t)g.prompt_len + (int64_t)g.n_resp * g.resp_len;
-    if (T > kMaxRows || rows + T > kMaxRows) return DUALKV_ERR_UNSUPPORTED;
+    if (T > kMaxRows || r + T > kMaxRows) return DUALKV_ERR_UNSUPPORTED;
+    r += T;
+  }
+  *rows = r;
+  return DUALKV_OK;
+}
+
+namespace {
+
+// Validate the groups and fill `G` and the row counts of `pr` (N, P, R, T
+// of group 0; Tld of the whole launch).
+int validate_groups(const dualkv_group* groups, int32_t n, Problem* pr, Groups* G) {
+  int64_t total;
+  const int st = check_groups(groups, n, &total);
+  if (st != DUALKV_OK) return st;
+  int64_t rows = 0, vl = 0;
+  G->n = n;
+  for (int i = 0; i < n; ++i) {
+    const dualkv_group& g = groups[i];
+    const int64_t T = (int64_t)g.prompt_len + (int64_t)g.n_resp * g.resp_len;
     G->N[i] = g.n_resp;
     G->P[i] = g.prompt_len;
     G->R[i] = g.resp_len;

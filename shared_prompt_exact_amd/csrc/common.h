@@ -110,6 +110,10 @@ static inline hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 g
   return e;
 }
 
+// Validates a group table (1..kMaxGroups well-formed entries, at most
+// 2^30 packed rows); returns a DUALKV_* status and the packed row count.
+int check_groups(const dualkv_group* groups, int32_t n, int64_t* rows);
+
 // ---- launchers implemented in the kernel translation units -------------
 hipError_t launch_repack(const void* src, void* dst, int64_t row_bytes, int N, int P, int R,
                          int direction, hipStream_t stream);

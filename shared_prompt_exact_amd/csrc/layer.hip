@@ -122,7 +122,7 @@ int layer_setup(const dualkv_layer_params* lp, const dualkv_group* groups, int32
     return DUALKV_ERR_INVALID_ARGUMENT;
   if (!(lp->rope_base > 1.f) || !isfinite(lp->rope_base) || !(lp->norm_eps > 0.f) || !isfinite(lp->norm_eps))
     return DUALKV_ERR_INVALID_ARGUMENT;
-  if (lp->head_dim % 2 != 0) return DUALKV_ERR_INVALID_ARGUMENT;
+  if (lp->head_dim % 2 != 0 || lp->n_q_heads % lp->n_kv_heads != 0) return DUALKV_ERR_INVALID_ARGUMENT;
   // GEMM tiles: every feature width a whole number of 128-wide blocks
   if (lp->hidden % 128 || lp->ffn % 128 || (lp->n_q_heads * lp->head_dim) % 128 ||
       (lp->n_kv_heads * lp->head_dim) % 128)
@@ -137,12 +137,11 @@ int layer_setup(const dualkv_layer_params* lp, const dualkv_group* groups, int32
   ap->dtype = DUALKV_BF16;
   ap->impl = DUALKV_IMPL_AUTO;
   ap->resp_valid_len = lp->resp_valid_len;
-  // validates heads and groups, and gives the packed row count
-  const size_t ws = dualkv_bwd_groups_workspace_bytes(ap, groups, n_groups);
-  if (ws == 0) return DUALKV_ERR_INVALID_ARGUMENT;
   int64_t T = 0;
-  for (int i = 0; i < n_groups; ++i)
-    T += (int64_t)groups[i].prompt_len + (int64_t)groups[i].n_resp * groups[i].resp_len;
+  const int st = check_groups(groups, n_groups, &T);
+  if (st != DUALKV_OK) return st;
+  // the attention's own checks (heads, head dim) on a non-empty batch
+  if (T > 0 && dualkv_bwd_groups_workspace_bytes(ap, groups, n_groups) == 0) return DUALKV_ERR_INVALID_ARGUMENT;
   if (T * std::max(lp->ffn, lp->hidden) >= ((int64_t)1 << 40)) return DUALKV_ERR_UNSUPPORTED;
   s->T = (int)T;
   s->Hm = lp->hidden;
@@ -217,17 +216,15 @@ int dualkv_rmsnorm_bwd(int32_t T, int32_t H, const void* x, const void* w, const
 
 int dualkv_rope(const dualkv_group* groups, int32_t n_groups, int32_t n_heads, int32_t head_dim, float base,
                 int32_t inverse, void* x, void* stream) {
-  dualkv_params ap{};
-  ap.n_q_heads = ap.n_kv_heads = n_heads;
-  ap.head_dim = head_dim;
-  ap.dtype = DUALKV_BF16;
-  ap.impl = DUALKV_IMPL_SCALAR;
   if (n_heads < 1 || head_dim < 2 || head_dim % 2 != 0 || !(base > 1.f) || !isfinite(base))
     return DUALKV_ERR_INVALID_ARGUMENT;
   if (inverse != 0 && inverse != 1) return DUALKV_ERR_INVALID_ARGUMENT;
-  if (dualkv_bwd_groups_workspace_bytes(&ap, groups, n_groups) == 0) return DUALKV_ERR_INVALID_ARGUMENT;
+  int64_t rows = 0;
+  const int st = check_groups(groups, n_groups, &rows);
+  if (st != DUALKV_OK) return st;
+  if (rows * n_heads * head_dim >= ((int64_t)1 << 40)) return DUALKV_ERR_UNSUPPORTED;
   const Groups G = groups_of(groups, n_groups);
-  const int T = G.row0[n_groups - 1] + G.P[n_groups - 1] + G.N[n_groups - 1] * G.R[n_groups - 1];
+  const int T = (int)rows;
   if (T == 0) return DUALKV_OK;
   if (x == nullptr) return DUALKV_ERR_INVALID_ARGUMENT;
   return status_of(launch_rope(T, n_heads, head_dim, G, base, inverse, x, static_cast<hipStream_t>(stream)));

@@ -162,3 +162,54 @@ def test_group_workspace_covers_every_row():
         a1, _ = group_array(g)
         sep += lib.dualkv_bwd_groups_workspace_bytes(ctypes.byref(p), a1, 1)
     assert both <= sep + 1024
+
+
+def layer_params(**kw):
+    base = dict(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=384, window=0, rope_base=1e4,
+                norm_eps=1e-6, valid_len=None)
+    base.update(kw)
+    return dk.make_layer_params(**base)
+
+
+def test_layer_argument_checks():
+    lib = dk.load_library()
+    arr, n = group_array((2, 30, 20))
+    ok = layer_params()
+    assert lib.dualkv_layer_saved_bytes(ctypes.byref(ok), arr, n) > 0
+    assert lib.dualkv_layer_workspace_bytes(ctypes.byref(ok), arr, n) > 0
+    for bad in (dict(hidden=200), dict(ffn=100), dict(head_dim=48)):        # not whole 128-wide blocks
+        p = layer_params(**bad)
+        w = dk.LayerWeights()
+        assert lib.dualkv_layer_fwd(ctypes.byref(p), arr, n, ctypes.byref(w), None, None, None, 0, None) == 2, bad
+    for bad in (dict(rope_base=1.0), dict(norm_eps=0.0), dict(n_kv_heads=3)):
+        p = layer_params(**bad)
+        w = dk.LayerWeights()
+        assert lib.dualkv_layer_fwd(ctypes.byref(p), arr, n, ctypes.byref(w), None, None, None, 0, None) == 1, bad
+        assert lib.dualkv_layer_saved_bytes(ctypes.byref(p), arr, n) == 0
+    w = dk.LayerWeights()
+    assert lib.dualkv_layer_fwd(ctypes.byref(ok), None, 1, ctypes.byref(w), None, None, None, 0, None) == 1
+    need = lib.dualkv_layer_saved_bytes(ctypes.byref(ok), arr, n)
+    d = ctypes.c_void_p(0x1000)
+    assert lib.dualkv_layer_fwd(ctypes.byref(ok), arr, n, ctypes.byref(w), d, d, d, need - 1, None) == 3
+    empty, ne = group_array((2, 0, 0))                                        # nothing to compute
+    assert lib.dualkv_layer_fwd(ctypes.byref(ok), empty, ne, ctypes.byref(w), None, None, None, 0, None) == 0
+
+
+def test_layer_op_argument_checks():
+    lib = dk.load_library()
+    d = ctypes.c_void_p(0x1000)
+    # GEMM: both operands transposed; k not a whole 64-wide block; k-major B with ragged n
+    assert lib.dualkv_gemm_bf16(1, 1, 128, 128, 64, d, 128, d, 64, d, 128, None, 0, None) == 2
+    assert lib.dualkv_gemm_bf16(0, 0, 100, 128, 70, d, 70, d, 128, d, 128, None, 0, None) == 2
+    assert lib.dualkv_gemm_bf16(0, 0, 100, 100, 64, d, 64, d, 100, d, 100, None, 0, None) == 2
+    assert lib.dualkv_gemm_bf16(2, 0, 100, 128, 64, d, 64, d, 128, d, 128, None, 0, None) == 1
+    assert lib.dualkv_gemm_bf16(0, 0, 100, 128, 64, ctypes.c_void_p(0x1008), 64, d, 128, d, 128, None, 0,
+                                None) == 1                                    # A not 16-byte aligned
+    assert lib.dualkv_gemm_bf16(0, 0, 0, 128, 64, None, 64, None, 128, None, 128, None, 0, None) == 0
+    assert lib.dualkv_rmsnorm_fwd(10, 12, 1e-6, d, d, d, d, None) == 1       # H % 8
+    assert lib.dualkv_rmsnorm_fwd(10, 16, 0.0, d, d, d, d, None) == 1        # eps
+    assert lib.dualkv_swiglu_fwd(12, d, d, d, None) == 1                      # n % 8
+    arr, n = group_array((2, 3, 4))
+    assert lib.dualkv_rope(arr, n, 2, 7, 1e4, 0, d, None) == 1                # odd head dim
+    assert lib.dualkv_rope(arr, n, 2, 8, 1e4, 2, d, None) == 1                # inverse flag
+    assert lib.dualkv_rope(None, 1, 2, 8, 1e4, 0, d, None) == 1
