@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdualkv.so")
-SOURCES = ["repack.hip", "attn_scalar.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "api.hip", "profile.hip",
+SOURCES = ["repack.hip", "attn_scalar.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq.hip", "api.hip", "profile.hip",
            "gemm.hip", "layer_ops.hip", "layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,347 @@
+// dQ kernel of the shared-prompt attention backward on gfx950 matrix cores
+// (its own translation unit, so that its register allocation and that of
+// the dK/dV kernel do not perturb each other).
+//
+// "DualKV: Shared-Prompt Flash Attention ..." (arXiv 2605.15422), Abstract:
+// the backward iterates over the same two disjoint key regions as the
+// forward.  Per visible (query i, key j) pair of a head, with
+// p = exp(scale*q.k - LSE_i) and Delta_i = dO_i . O_i: dp = dO_i . v_j,
+// ds = p (dp - Delta_i), dQ_i += scale ds k_j.  Query-parallel with the
+// forward's tiling (K, V row-major in LDS, read transposed for K^T; Q^T and
+// dO^T in registers); S and dP are recomputed; dQ accumulates in registers
+// and is written once, so no atomics and no fp32 dQ buffer.
+#include "lds_tiles.h"
+
+namespace dualkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+// Ring slot of a tile: a compile-time constant (IntC) on the unrolled path,
+// a runtime value otherwise.
+template <int V>
+__device__ __forceinline__ constexpr int slot_value(IntC<V>) { return V; }
+__device__ __forceinline__ int slot_value(int x) { return x; }
+
+// ----------------------------------------------------------------- dq kernel
+
+template <int D, int BN, int NW, int NS, int DS>
+struct DqCfg {
+  static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
+  static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 32 * 4 : 0;   // partial S, dP of a 32-key sub-tile
+  static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
+  static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
+  static constexpr int BPW = KBLK / NW;
+  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
+};
+
+// DS = 2: a wave pair owns the same 32 query rows, each half of the head
+// dim (Q^T, dO^T, the contractions and the dQ accumulator); partial S and
+// dP meet in LDS and are summed in the same order by both waves.
+template <int D, int BN, int NW, int NS, int DS>
+__global__ void __launch_bounds__(NW * 64)
+    bwd_dq_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
+                  const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                  const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                  const float* __restrict__ delta, uint16_t* __restrict__ dq) {
+  using C = DqCfg<D, BN, NW, NS, DS>;
+  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dh = wave % DS, wq = wave / DS;
+  const int BM = 32 * NWQ / HG;
+  const int NB = GB.off[G.n];                 // row blocks of all groups, per head group
+  const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
+  if (L < 0) return;                          // grid padding (whole workgroup)
+  const int hgi = L / NB;
+  const int gi = group_of(GB.off, G.n, L % NB);
+  const int blk = L % NB - GB.off[gi];
+  const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    dout += r0 * pr.Hq * D;
+    dq += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    lse += r0;
+    delta += r0;
+  }
+  const int gpw = pr.g / HG;
+  const int c = hgi / gpw;
+  const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
+  const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
+
+  const int wr0 = b.r0 + (wq / HG) * 32;
+  const int my_r = wr0 + l32;
+  const bool qvalid = my_r < b.nvalid;
+  const int qpos = b.posoff + my_r;
+  const int64_t qrow = (int64_t)b.base + my_r;
+  const int64_t ostride = (int64_t)pr.Hq * D;
+  const int blk_hi = min(b.r0 + BM, b.nvalid) - 1;
+  const int w_hi = min(wr0 + 31, b.nvalid - 1);
+  const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
+  const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
+
+  bf16x8 qB[KTH], doB[KTH];
+#pragma unroll
+  for (int kk = 0; kk < KTH; ++kk) {
+    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (qvalid) {
+      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * (dh * KTH + kk) + 8 * hf;
+      z = *reinterpret_cast<const uint4*>(q + off);
+      y = *reinterpret_cast<const uint4*>(dout + off);
+    }
+    qB[kk] = __builtin_bit_cast(bf16x8, z);
+    doB[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  float lse2 = INFINITY, dlt = 0.f;   // +inf: p = 0 for rows without keys
+  if (qvalid) {
+    const float Lr = lse[(int64_t)h * pr.Tld + qrow];
+    lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
+    dlt = delta[(int64_t)h * pr.Tld + qrow];
+  }
+  wait_vmcnt<0>();                    // the loop's waits count only tile loads
+  asm volatile("" ::: "memory");
+  const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
+
+  f32x16 acc[DBH];
+#pragma unroll
+  for (int db = 0; db < DBH; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float* const xch = reinterpret_cast<float*>(lds + NS * C::STAGE);   // DS > 1 only
+
+  if (blk_hi >= b.r0) {
+    const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
+    const int ntiles = tr.nA + tr.nB;
+    const int64_t rs = (int64_t)pr.Hkv * D;
+    auto issue = [&](int t) {
+      const KeyTile kt = tile_at(pr, b, tr, t, BN);
+      const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
+      uint16_t* slot = lds + (t % NS) * C::STAGE;
+      const int nv = min(BN, kt.lim);
+      dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
+      dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < ntiles) issue(t);
+    // One key tile.  Where the loop below is unrolled by NS the ring slot is
+    // a compile-time constant, so LDS addresses are per-lane bases plus
+    // immediates.
+    auto step = [&](int it, auto slot_c) {
+      const int SLOT = slot_value(slot_c);
+      if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
+      else wait_vmcnt<0>();
+      block_sync();
+      if (it + NS - 1 < ntiles) issue(it + NS - 1);
+      const KeyTile kt = tile_at(pr, b, tr, it, BN);
+      const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      const uint16_t* Ks = lds + SLOT * C::STAGE;
+      const uint16_t* Vs = Ks + C::K_ELEMS;
+      // 32-key sub-tiles one after the other: a BN-key tile costs one
+      // barrier, the registers of one 32-key sub-tile
+#pragma unroll
+      for (int kb = 0; kb < NB32; ++kb) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        if (kind != 0) {
+          if constexpr (KTH <= 8) {
+            // the two operand reads of k-step kk+1 are issued before the
+            // two MFMAs of step kk (scheduling fences keep them there), so
+            // their latency overlaps MFMA work
+            bf16x8 ka = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
+            bf16x8 va = row_operand<D>(Vs, kb * 32 + l32, dh * KTH, hf);
+#pragma unroll
+            for (int kk = 0; kk < KTH; ++kk) {
+              bf16x8 kn = ka, vn = va;
+              if (kk + 1 < KTH) {
+                kn = row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk + 1, hf);
+                vn = row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk + 1, hf);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              s = mfma32(ka, qB[kk], s);
+              dp = mfma32(va, doB[kk], dp);
+              __builtin_amdgcn_sched_barrier(0);
+              ka = kn;
+              va = vn;
+            }
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < KTH; ++kk) {
+              s = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s);
+              dp = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp);
+              if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        if constexpr (DS > 1) {
+          // partial S and dP of the DS waves sharing these rows meet in LDS;
+          // every wave adds the DS partials in index order (its own from
+          // registers), so all of them hold bit-identical sums.  Layout
+          // [wave][float4 j][lane] (S in j = 0..3, dP in 4..7): each 16-byte
+          // access of a wave covers 1 KiB contiguous (no bank conflicts).
+          float4* const x4 = reinterpret_cast<float4*>(xch);
+          if (kind != 0)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              x4[(wave * 8 + i4) * 64 + lane] = make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
+              x4[(wave * 8 + 4 + i4) * 64 + lane] =
+                  make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
+            }
+          block_sync();
+          if (kind != 0)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
+#pragma unroll
+              for (int pp = 0; pp < DS; ++pp) {
+                const int w = wave - dh + pp;
+                const float4 vs = pp == dh ? make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3])
+                                           : x4[(w * 8 + i4) * 64 + lane];
+                const float4 vd = pp == dh ? make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3])
+                                           : x4[(w * 8 + 4 + i4) * 64 + lane];
+                if (pp == 0) {
+                  ts4 = vs;
+                  td4 = vd;
+                } else {
+                  ts4.x += vs.x; ts4.y += vs.y; ts4.z += vs.z; ts4.w += vs.w;
+                  td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
+                }
+              }
+              s[4 * i4] = ts4.x; s[4 * i4 + 1] = ts4.y; s[4 * i4 + 2] = ts4.z; s[4 * i4 + 3] = ts4.w;
+              dp[4 * i4] = td4.x; dp[4 * i4 + 1] = td4.y; dp[4 * i4 + 2] = td4.z; dp[4 * i4 + 3] = td4.w;
+            }
+          if (kb + 1 < NB32) block_sync();     // partials read before the next sub-tile's
+        }
+        if (kind != 0) {
+          if (kind == 2) {
+            // hidden scores become -inf: p = exp2(-inf - lse2) = 0 below
+            int d0 = qpos - kt.pos0 - 4 * hf - kb * 32;
+            int lim0 = (qvalid ? kt.lim : 0) - 4 * hf - kb * 32;
+            asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kc = 8 * (i >> 2) + (i & 3);
+              const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+              s[i] = vis ? s[i] : -INFINITY;
+            }
+          }
+          bf16x8 dsB[2];
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * hs + j;
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
+              dsB[hs][j] = (__bf16)(p * (dp[i] - dlt));
+            }
+          if constexpr (DBH <= 4) {
+            // k-step outer (independent accumulators back to back), each K^T
+            // operand read one MFMA ahead (scheduling fences hold the order)
+            bf16x8 cur = trans_operand<D>(Ks, 0, dh * DBH * 32, 2 * kb, lane);
+#pragma unroll
+            for (int x = 0; x < 2 * DBH; ++x) {
+              const int hs = x / DBH, db = x % DBH;
+              bf16x8 nxt = cur;
+              if (x + 1 < 2 * DBH) {
+                nxt = trans_operand<D>(Ks, 0, (dh * DBH + (x + 1) % DBH) * 32, 2 * kb + (x + 1) / DBH, lane);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              acc[db] = mfma32(cur, dsB[hs], acc[db]);
+              __builtin_amdgcn_sched_barrier(0);
+              cur = nxt;
+            }
+          } else {
+#pragma unroll
+            for (int db = 0; db < DBH; ++db) {
+#pragma unroll
+              for (int hs = 0; hs < 2; ++hs)
+                acc[db] = mfma32(trans_operand<D>(Ks, 0, (dh * DBH + db) * 32, 2 * kb + hs, lane), dsB[hs],
+                                 acc[db]);
+              if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+    };
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    if constexpr (D <= 128) {
+      // unrolled by the ring depth (small head dims: registers to spare)
+      int it = 0;
+      for (; it + NS <= ntiles; it += NS) {
+        step(it, IntC<0>{});
+        step(it + 1, IntC<1>{});
+        if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
+        if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
+      }
+      if (it < ntiles) step(it, IntC<0>{});
+      if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
+      if constexpr (NS == 4)
+        if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
+    } else {
+      for (int it = 0; it < ntiles; ++it) step(it, it % NS);
+    }
+  }
+
+  if (my_r < b.seglen) {
+    uint16_t* orow = dq + qrow * ostride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        union { __bf16 h[4]; uint2 u; } pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
+        *reinterpret_cast<uint2*>(orow + (dh * DBH + db) * 32 + 8 * g4 + 4 * hf) = pk.u;
+      }
+  }
+}
+
+
+}  // namespace
+
+template <int D, int BN, int NW, int NS, int DS>
+hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
+                         const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                         const float* lse, const float* delta, uint16_t* dq, hipStream_t stream) {
+  using C = DqCfg<D, BN, NW, NS, DS>;
+  static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = allow_lds(bwd_dq_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  return launch("bwd_dq", bwd_dq_kernel<D, BN, NW, NS, DS>, dim3((unsigned)nwg), dim3(NW * 64), C::LDS_BYTES,
+                stream, pr, G, gb, HG, q, k, v, dout, lse, delta, dq);
+}
+
+// the configurations the backward dispatch uses
+template hipError_t launch_bwd_dq<64, 64, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+                                                   const uint16_t*, const uint16_t*, const uint16_t*,
+                                                   const uint16_t*, const float*, const float*, uint16_t*,
+                                                   hipStream_t);
+template hipError_t launch_bwd_dq<128, 32, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+                                                    const uint16_t*, const uint16_t*, const uint16_t*,
+                                                    const uint16_t*, const float*, const float*, uint16_t*,
+                                                    hipStream_t);
+template hipError_t launch_bwd_dq<256, 32, 4, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+                                                    const uint16_t*, const uint16_t*, const uint16_t*,
+                                                    const uint16_t*, const float*, const float*, uint16_t*,
+                                                    hipStream_t);
+template hipError_t launch_bwd_dq<512, 32, 4, 2, 2>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+                                                    const uint16_t*, const uint16_t*, const uint16_t*,
+                                                    const uint16_t*, const float*, const float*, uint16_t*,
+                                                    hipStream_t);
+
+}  // namespace dualkv
