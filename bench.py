@@ -214,7 +214,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention "
               "layer is sharded across GPUs by data parallelism over prompt groups, "
-              "see DESIGN.md", file=sys.stderr)
+              "each GPU running this library on its own micro-batches", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

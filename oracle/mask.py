@@ -6,7 +6,7 @@ from N(P+R) rows into P+NR rows; attention for a response query runs over
 two disjoint key regions, the shared prompt and that response's own
 tokens, and prompt queries see the prompt only (causal masking).
 
-Readings where the abstract is silent (listed in the design doc as well):
+Readings where the abstract is silent:
 * packed row order: prompt rows 0..P-1, then response n at rows
   P+nR .. P+nR+R-1 for n = 0..N-1;
 * a response token r has logical position P+r; causal order and the

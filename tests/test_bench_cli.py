@@ -1,6 +1,6 @@
 """bench.py's command line on the CPU: more than one GPU is refused with a
 message (the attention layer shards by data parallelism over prompt groups;
-this build measures one GPU)."""
+the benchmark measures one GPU)."""
 import os
 import subprocess
 import sys
