@@ -48,8 +48,9 @@ template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
     bwd_dq_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                  const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-                  const float* __restrict__ delta, uint16_t* __restrict__ dq) {
+                  const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
+                  const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ lse2w,
+                  uint16_t* __restrict__ dq) {
   using C = DqCfg<D, BN, NW, NS, DS>;
   constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
   constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
@@ -71,7 +72,9 @@ __global__ void __launch_bounds__(NW * 64)
     const int64_t r0 = G.row0[gi];
     q += r0 * pr.Hq * D;
     dout += r0 * pr.Hq * D;
+    o += r0 * pr.Hq * D;
     dq += r0 * pr.Hq * D;
+    lse2w += r0;
     k += r0 * pr.Hkv * D;
     v += r0 * pr.Hkv * D;
     lse += r0;
@@ -106,7 +109,33 @@ __global__ void __launch_bounds__(NW * 64)
     doB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   float lse2 = INFINITY, dlt = 0.f;   // +inf: p = 0 for rows without keys
-  if (qvalid) {
+  if constexpr (DS == 1) {
+    // Delta = dO . O of this row: the lane's half of the head dim (the same
+    // elements as its dO^T operands), then the partner lane's half, added in
+    // the same order in both lanes.  Written with LSE*log2(e) for the dK/dV
+    // kernel; rows without keys get Delta = 0, LSE2 = +inf.
+    float part = 0.f;
+    if (qvalid) {
+#pragma unroll
+      for (int kk = 0; kk < KTH; ++kk) {
+        const bf16x8 ov = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(o + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part = fmaf((float)ov[j], (float)doB[kk][j], part);
+      }
+    }
+    const float other = swap_halves(part);
+    const float full = hf == 0 ? part + other : other + part;
+    if (qvalid) {
+      const float Lr = lse[(int64_t)h * pr.Tld + qrow];
+      lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
+      dlt = Lr == -INFINITY ? 0.f : full;
+    }
+    if (hf == 0 && my_r < b.seglen) {
+      delta[(int64_t)h * pr.Tld + qrow] = dlt;
+      lse2w[(int64_t)h * pr.Tld + qrow] = lse2;
+    }
+  } else if (qvalid) {
     const float Lr = lse[(int64_t)h * pr.Tld + qrow];
     lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
     dlt = delta[(int64_t)h * pr.Tld + qrow];
@@ -317,31 +346,32 @@ __global__ void __launch_bounds__(NW * 64)
 template <int D, int BN, int NW, int NS, int DS>
 hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
                          const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                         const float* lse, const float* delta, uint16_t* dq, hipStream_t stream) {
+                         const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
+                         hipStream_t stream) {
   using C = DqCfg<D, BN, NW, NS, DS>;
   static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
   static const hipError_t attr = allow_lds(bwd_dq_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   return launch("bwd_dq", bwd_dq_kernel<D, BN, NW, NS, DS>, dim3((unsigned)nwg), dim3(NW * 64), C::LDS_BYTES,
-                stream, pr, G, gb, HG, q, k, v, dout, lse, delta, dq);
+                stream, pr, G, gb, HG, q, k, v, dout, o, lse, delta, lse2, dq);
 }
 
 // the configurations the backward dispatch uses
 template hipError_t launch_bwd_dq<64, 64, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                    const uint16_t*, const uint16_t*, const uint16_t*,
-                                                   const uint16_t*, const float*, const float*, uint16_t*,
-                                                   hipStream_t);
+                                                   const uint16_t*, const uint16_t*, const float*, float*, float*,
+                                                   uint16_t*, hipStream_t);
 template hipError_t launch_bwd_dq<128, 32, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const uint16_t*, const float*, const float*, uint16_t*,
-                                                    hipStream_t);
+                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
+                                                    uint16_t*, hipStream_t);
 template hipError_t launch_bwd_dq<256, 32, 4, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const uint16_t*, const float*, const float*, uint16_t*,
-                                                    hipStream_t);
+                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
+                                                    uint16_t*, hipStream_t);
 template hipError_t launch_bwd_dq<512, 32, 4, 2, 2>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const uint16_t*, const float*, const float*, uint16_t*,
-                                                    hipStream_t);
+                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
+                                                    uint16_t*, hipStream_t);
 
 }  // namespace dualkv

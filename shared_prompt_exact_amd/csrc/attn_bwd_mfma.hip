@@ -751,7 +751,9 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const uint16_t* do16 = static_cast<const uint16_t*>(dout);
   hipError_t e;
-  {
+  if constexpr (DS > 1) {
+    // the dQ kernel splits rows over wave pairs: Delta and LSE2 come from
+    // their own kernel (with DS == 1 the dQ kernel forms them)
     constexpr int RPB = 4 * 64 / (D / 8);   // rows per 256-thread block
     const int64_t nrows = (int64_t)pr.Tld * pr.Hq;
     e = launch("bwd_delta", delta_lse2_kernel<D>, dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0,
@@ -759,7 +761,8 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_dq > 0) {
-    e = launch_bwd_dq<D, kDqBN, NW, DQNS, DS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16, lse, delta,
+    e = launch_bwd_dq<D, kDqBN, NW, DQNS, DS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16,
+                                               static_cast<const uint16_t*>(o), lse, delta, lse2,
                                                static_cast<uint16_t*>(dq), stream);
     if (e != hipSuccess) return e;
   }

@@ -138,11 +138,15 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
                            void* dq, void* dk, void* dv, void* workspace, hipStream_t stream);
 
 // dQ kernel of the MFMA backward (attn_bwd_dq.hip), for the configurations
-// the dispatch in attn_bwd_mfma.hip uses.
+// the dispatch in attn_bwd_mfma.hip uses.  With DS == 1 (a wave holds whole
+// rows) the kernel also forms Delta = rowsum(dO*O) of its rows and writes it
+// with LSE*log2(e) (+inf where LSE = -inf) to `delta` and `lse2`; with
+// DS > 1 it reads `delta`, written beforehand by the Delta kernel.
 template <int D, int BN, int NW, int NS, int DS>
 hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
                          const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                         const float* lse, const float* delta, uint16_t* dq, hipStream_t stream);
+                         const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
+                         hipStream_t stream);
 
 // Scalar backward: delta[h][t] = sum_d dO[t,h,d] * O[t,h,d] in fp32 (0 on
 // rows with no visible key) for all pr.Tld rows.
