@@ -30,15 +30,18 @@
 namespace dualkv {
 namespace {
 
-constexpr int GBN = 128, GBK = 64;
+constexpr int GBK = 64;
 
-// Tile of BM x 128 (BM = 128: four waves, a two-slot ring, two workgroups
-// per CU; BM = 256: eight waves, a three-slot ring, one workgroup per CU,
-// tile loads two k-steps ahead).
-template <int BM>
+// Tile of BM x 64*WN: waves of 64 x 32*WN (WN = 2: BM = 128 with four waves,
+// a two-slot ring and two workgroups per CU, or BM = 256 with eight waves
+// and a three-slot ring, tile loads two k-steps ahead; WN = 4: 256 x 256
+// with eight waves of 64 x 128 and a two-slot ring, eight MFMAs per six
+// operand reads).
+template <int BM, int WN>
 struct GemmCfg {
-  static constexpr int NW = BM / 32;              // waves, each a 64 x 64 quadrant
-  static constexpr int NS = BM == 256 ? 3 : 2;    // ring slots
+  static constexpr int GBN = 64 * WN;             // columns of C per workgroup
+  static constexpr int NW = BM / 32;              // waves, each 64 x 32*WN
+  static constexpr int NS = (BM == 256 && WN == 2) ? 3 : 2;    // ring slots
   static constexpr int A_ELEMS = BM * GBK, B_ELEMS = GBN * GBK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS = NS * STAGE * 2;      // bytes
@@ -59,17 +62,17 @@ __device__ __forceinline__ bf16x8 kslot_row_operand(const uint16_t* tile, int ro
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <bool TA, bool TB, int BM>
+template <bool TA, bool TB, int BM, int WN>
 __global__ void __launch_bounds__(BM * 2)
     gemm_bf16_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
                      const uint16_t* __restrict__ B, int64_t ldb, uint16_t* C, int64_t ldc,
                      const uint16_t* R, int64_t ldr, int tiles_n) {
-  using G = GemmCfg<BM>;
-  constexpr int NS = G::NS;
+  using G = GemmCfg<BM, WN>;
+  constexpr int NS = G::NS, GBN = G::GBN;
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;     // 64 x 64 quadrant of the wave
+  const int wm = wave >> 1, wn = wave & 1;     // 64 x 32*WN block of the wave
   const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
   const int m0 = bm * BM, n0 = bn * GBN;
   const int nk = (K + GBK - 1) / GBK;
@@ -89,11 +92,11 @@ __global__ void __launch_bounds__(BM * 2)
       dma_rows<GBN>(B + (int64_t)k0 * ldb + n0, ldb, min(GBK, K - k0), Bs, wave * G::BPW, G::BPW, lane);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][WN];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -124,20 +127,23 @@ __global__ void __launch_bounds__(BM * 2)
     }
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[2], b[WN];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int mr = wm * 64 + i * 32;
         if constexpr (TA) a[i] = trans_operand<BM>(As, 0, mr, ks, lane);
         else a[i] = kslot_row_operand(As, mr + l32, ks, hf);
-        const int nr = wn * 64 + i * 32;
-        if constexpr (TB) b[i] = kslot_row_operand(Bs, nr + l32, ks, hf);
-        else b[i] = trans_operand<GBN>(Bs, 0, nr, ks, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int nr = wn * 32 * WN + j * 32;
+        if constexpr (TB) b[j] = kslot_row_operand(Bs, nr + l32, ks, hf);
+        else b[j] = trans_operand<GBN>(Bs, 0, nr, ks, lane);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
     }
   }
 
@@ -145,8 +151,8 @@ __global__ void __launch_bounds__(BM * 2)
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + l32;
+    for (int j = 0; j < WN; ++j) {
+      const int n = n0 + wn * 32 * WN + j * 32 + l32;
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -160,24 +166,32 @@ __global__ void __launch_bounds__(BM * 2)
     }
 }
 
-template <bool TA, bool TB, int BM>
+template <bool TA, bool TB, int BM, int WN>
 hipError_t run_gemm(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                     int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
-  using G = GemmCfg<BM>;
+  using G = GemmCfg<BM, WN>;
   static_assert(G::LDS <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = allow_lds(gemm_bf16_kernel<TA, TB, BM>, G::LDS);
+  static const hipError_t attr = allow_lds(gemm_bf16_kernel<TA, TB, BM, WN>, G::LDS);
   if (attr != hipSuccess) return attr;
-  const int tm = (M + BM - 1) / BM, tn = (N + GBN - 1) / GBN;
-  return launch("gemm", gemm_bf16_kernel<TA, TB, BM>, dim3((unsigned)(tm * tn)), dim3(BM * 2), G::LDS, stream, M,
+  const int tm = (M + BM - 1) / BM, tn = (N + G::GBN - 1) / G::GBN;
+  return launch("gemm", gemm_bf16_kernel<TA, TB, BM, WN>, dim3((unsigned)(tm * tn)), dim3(BM * 2), G::LDS, stream, M,
                 N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
                 static_cast<uint16_t*>(C), ldc, static_cast<const uint16_t*>(R), ldr, tn);
 }
+
+constexpr int GBN = 128;   // the narrowest tile's columns: the shape rules below
 
 // The 256-row tile where the rows allow it: whole 256-row blocks when A is
 // k-major; otherwise enough rows that 256-row blocks fill the chip.
 bool use_tall(bool ta, int M, int N) {
   if (ta) return M % 256 == 0;
   return (int64_t)((M + 255) / 256) * ((N + GBN - 1) / GBN) >= 512;
+}
+
+// The 256 x 256 tile: a tall tile whose columns come in whole 256-wide
+// blocks, with at least one block per CU.
+bool use_wide(bool ta, int M, int N) {
+  return use_tall(ta, M, N) && N % 256 == 0 && (int64_t)((M + 255) / 256) * (N / 256) >= 256;
 }
 
 }  // namespace
@@ -202,15 +216,18 @@ hipError_t launch_gemm(bool ta, bool tb, int M, int N, int K, const void* A, int
                        int64_t ldb, void* C, int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (ta && tb) return hipErrorInvalidValue;
-  const bool tall = use_tall(ta, M, N);
+  const bool tall = use_tall(ta, M, N), wide = use_wide(ta, M, N);
   if (ta)
-    return tall ? run_gemm<true, false, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-                : run_gemm<true, false, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+    return wide ? run_gemm<true, false, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+         : tall ? run_gemm<true, false, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+                : run_gemm<true, false, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
   if (tb)
-    return tall ? run_gemm<false, true, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-                : run_gemm<false, true, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
-  return tall ? run_gemm<false, false, 256>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-              : run_gemm<false, false, 128>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+    return wide ? run_gemm<false, true, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+         : tall ? run_gemm<false, true, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+                : run_gemm<false, true, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+  return wide ? run_gemm<false, false, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+       : tall ? run_gemm<false, false, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
+              : run_gemm<false, false, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
 }
 
 }  // namespace dualkv

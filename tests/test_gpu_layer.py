@@ -49,6 +49,9 @@ def tight(name, got, want, rel=2e-3):
     (1, 0, 256, 384, 200, False), (1, 0, 128, 128, 64, True), (1, 0, 384, 256, 1001, False),
     # enough 256-row blocks for the eight-wave tile in the row-major forms
     (0, 0, 4000, 4096, 256, True), (0, 1, 4000, 4096, 128, False),
+    # 256 x 256 tiles (256-wide column blocks, at least one block per CU), a ragged last row block
+    # and, in the weight-gradient form, a ragged k
+    (0, 0, 4000, 4096, 192, True), (0, 1, 4096, 4096, 128, False), (1, 0, 4096, 4096, 1001, False),
 ])
 def test_gemm(ta, tb, M, N, K, res):
     print(f"gemm ta={ta} tb={tb} M={M} N={N} K={K} residual={res}", flush=True)
