@@ -63,10 +63,10 @@ struct FwdCfg {
   static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-// DS = 2 splits the head dim over a pair of waves (waves 2j, 2j+1 own the
-// same 32 query rows, each half of D for Q^T, the K contraction and the O
-// accumulator); their partial scores meet in LDS, S = S_lo + S_hi, summed in
-// the same order by both so they agree bit for bit.
+// DS > 1 splits the head dim over DS consecutive waves (they own the same
+// 32 query rows, each a 1/DS slice of D for Q^T, the K contraction and the O
+// accumulator); their partial scores meet in LDS and every one of them adds
+// the DS partials in head-dim order, so they agree bit for bit.
 template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
     fwd_mfma_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
@@ -205,12 +205,24 @@ __global__ void __launch_bounds__(NW * 64)
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const float4 t = x4[((wave ^ 1) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
-              // lower half first in both waves: identical sums
-              s[kb][4 * i4 + 0] = dh == 0 ? s[kb][4 * i4 + 0] + t.x : t.x + s[kb][4 * i4 + 0];
-              s[kb][4 * i4 + 1] = dh == 0 ? s[kb][4 * i4 + 1] + t.y : t.y + s[kb][4 * i4 + 1];
-              s[kb][4 * i4 + 2] = dh == 0 ? s[kb][4 * i4 + 2] + t.z : t.z + s[kb][4 * i4 + 2];
-              s[kb][4 * i4 + 3] = dh == 0 ? s[kb][4 * i4 + 3] + t.w : t.w + s[kb][4 * i4 + 3];
+              // the DS partials added in head-dim order by every wave (its own
+              // from registers): identical sums in all of them
+              float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+              for (int pp = 0; pp < DS; ++pp) {
+                const float4 v4 = pp == dh ? make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2],
+                                                         s[kb][4 * i4 + 3])
+                                           : x4[((wave - dh + pp) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
+                if (pp == 0) {
+                  t = v4;
+                } else {
+                  t.x += v4.x; t.y += v4.y; t.z += v4.z; t.w += v4.w;
+                }
+              }
+              s[kb][4 * i4 + 0] = t.x;
+              s[kb][4 * i4 + 1] = t.y;
+              s[kb][4 * i4 + 2] = t.z;
+              s[kb][4 * i4 + 3] = t.w;
             }
       }
       if (kind != 0) {
@@ -330,11 +342,13 @@ struct FwdPlan {
 FwdPlan plan(const Problem& pr, const Groups& G) {
   FwdPlan p;
   // Per wave, Q^T and the O accumulator take 3*D/4 registers: two waves per
-  // SIMD fit up to D = 128; D = 256 splits the head dim over wave pairs
-  // (still two per SIMD); D = 512 splits it and runs one wave per SIMD.
-  p.NW = pr.D <= 256 ? 8 : 4;
+  // SIMD fit up to D = 128; D = 256 splits the head dim over wave pairs and
+  // D = 512 over groups of four waves, so every head dim runs eight waves,
+  // two per SIMD (at D = 512 four-way instead of two-way with one wave per
+  // SIMD: 12% less forward time on the Gemma-style global layer).
+  p.NW = 8;
   p.BN = pr.D <= 128 ? 64 : 32;
-  p.DS = pr.D <= 128 ? 1 : 2;
+  p.DS = pr.D <= 128 ? 1 : pr.D == 256 ? 2 : 4;
   p.HG = heads_per_block(pr.g, p.NW / p.DS);
   p.BM = 32 * (p.NW / p.DS) / p.HG;
   int64_t nb = 0;
@@ -378,7 +392,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
     case 64: return run<64, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
     case 128: return run<128, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
     case 256: return run<256, 32, 8, 3, 2>(pr, G, p, q, k, v, o, lse, stream);
-    case 512: return run<512, 32, 4, 2, 2>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
+    case 512: return run<512, 32, 8, 2, 4>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
 }
