@@ -34,7 +34,11 @@ struct DqCfg {
   static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
   static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 32 * 4 : 0;   // partial S, dP of a 32-key sub-tile
+  // partial S and dP of a 32-key sub-tile: both at once, or (when LDS is
+  // short) S then dP through the same half-size buffer
+  static constexpr int XCH_FULL = DS > 1 ? NW * 64 * 32 * 4 : 0;
+  static constexpr bool XCH_TWO_PHASE = NS * STAGE * 2 + XCH_FULL > 160 * 1024;
+  static constexpr int XCH_BYTES = XCH_TWO_PHASE ? XCH_FULL / 2 : XCH_FULL;
   static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
   static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
   static constexpr int BPW = KBLK / NW;
@@ -221,39 +225,53 @@ __global__ void __launch_bounds__(NW * 64)
           // partial S and dP of the DS waves sharing these rows meet in LDS;
           // every wave adds the DS partials in index order (its own from
           // registers), so all of them hold bit-identical sums.  Layout
-          // [wave][float4 j][lane] (S in j = 0..3, dP in 4..7): each 16-byte
-          // access of a wave covers 1 KiB contiguous (no bank conflicts).
+          // [wave][float4 j][lane]: each 16-byte access of a wave covers
+          // 1 KiB contiguous (no bank conflicts).  One phase: S in j = 0..3,
+          // dP in 4..7; two phases: S, then dP, in j = 0..3 of a buffer half
+          // the size.
           float4* const x4 = reinterpret_cast<float4*>(xch);
-          if (kind != 0)
+          constexpr int J = C::XCH_TWO_PHASE ? 4 : 8;
+          auto put = [&](const f32x16& a, int j0) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              x4[(wave * J + j0 + i4) * 64 + lane] = make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
+          };
+          auto sum = [&](f32x16& a, int j0) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              x4[(wave * 8 + i4) * 64 + lane] = make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3]);
-              x4[(wave * 8 + 4 + i4) * 64 + lane] =
-                  make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
-            }
-          block_sync();
-          if (kind != 0)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              float4 ts4 = make_float4(0.f, 0.f, 0.f, 0.f), td4 = ts4;
+              float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
               for (int pp = 0; pp < DS; ++pp) {
-                const int w = wave - dh + pp;
-                const float4 vs = pp == dh ? make_float4(s[4 * i4], s[4 * i4 + 1], s[4 * i4 + 2], s[4 * i4 + 3])
-                                           : x4[(w * 8 + i4) * 64 + lane];
-                const float4 vd = pp == dh ? make_float4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3])
-                                           : x4[(w * 8 + 4 + i4) * 64 + lane];
+                const float4 v4 = pp == dh ? make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3])
+                                           : x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
                 if (pp == 0) {
-                  ts4 = vs;
-                  td4 = vd;
+                  t4 = v4;
                 } else {
-                  ts4.x += vs.x; ts4.y += vs.y; ts4.z += vs.z; ts4.w += vs.w;
-                  td4.x += vd.x; td4.y += vd.y; td4.z += vd.z; td4.w += vd.w;
+                  t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
                 }
               }
-              s[4 * i4] = ts4.x; s[4 * i4 + 1] = ts4.y; s[4 * i4 + 2] = ts4.z; s[4 * i4 + 3] = ts4.w;
-              dp[4 * i4] = td4.x; dp[4 * i4 + 1] = td4.y; dp[4 * i4 + 2] = td4.z; dp[4 * i4 + 3] = td4.w;
+              a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
             }
+          };
+          if constexpr (C::XCH_TWO_PHASE) {
+            if (kind != 0) put(s, 0);
+            block_sync();
+            if (kind != 0) sum(s, 0);
+            block_sync();                       // every wave has read the S partials
+            if (kind != 0) put(dp, 0);
+            block_sync();
+            if (kind != 0) sum(dp, 0);
+          } else {
+            if (kind != 0) {
+              put(s, 0);
+              put(dp, 4);
+            }
+            block_sync();
+            if (kind != 0) {
+              sum(s, 0);
+              sum(dp, 4);
+            }
+          }
           if (kb + 1 < NB32) block_sync();     // partials read before the next sub-tile's
         }
         if (kind != 0) {
@@ -369,7 +387,7 @@ template hipError_t launch_bwd_dq<256, 32, 4, 3, 1>(const Problem&, const Groups
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);
-template hipError_t launch_bwd_dq<512, 32, 4, 2, 2>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+template hipError_t launch_bwd_dq<512, 32, 8, 2, 4>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);

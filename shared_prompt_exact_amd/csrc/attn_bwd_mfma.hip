@@ -627,14 +627,14 @@ __global__ void __launch_bounds__(256)
 // most 256 dims of its operands and accumulators (VGPRs plus accumulation
 // registers), and the waves of a workgroup cover several 32-row (or
 // 32-key) slices that share each streamed tile.
-inline int dq_waves(int D) { return D <= 128 ? 8 : 4; }
+inline int dq_waves(int D) { return D == 256 ? 4 : 8; }
 inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
 // Key tiles per wave of the dK/dV kernel.  Two tiles (one wave per SIMD)
 // halve the LDS reads per MFMA but lose the second wave's latency hiding;
 // measured slower at D = 128 (11.6 ms against 9.9 ms on the Qwen3-8B-shaped
 // layer), so every head dim runs one tile per wave.
 inline int kv_tiles_per_wave(int) { return 1; }
-inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
+inline int dq_split(int D) { return D <= 256 ? 1 : 4; }
 inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
 struct BwdPlan {
@@ -803,7 +803,7 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
     case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 8, 4, 32, 2, 2, 4, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
