@@ -205,6 +205,15 @@ __global__ void __launch_bounds__(NW * 64)
           for (int kb = 0; kb < NB32; ++kb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
+              if constexpr (DS == 2) {
+                const float4 t = x4[((wave ^ 1) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
+                // lower half first in both waves: identical sums
+                s[kb][4 * i4 + 0] = dh == 0 ? s[kb][4 * i4 + 0] + t.x : t.x + s[kb][4 * i4 + 0];
+                s[kb][4 * i4 + 1] = dh == 0 ? s[kb][4 * i4 + 1] + t.y : t.y + s[kb][4 * i4 + 1];
+                s[kb][4 * i4 + 2] = dh == 0 ? s[kb][4 * i4 + 2] + t.z : t.z + s[kb][4 * i4 + 2];
+                s[kb][4 * i4 + 3] = dh == 0 ? s[kb][4 * i4 + 3] + t.w : t.w + s[kb][4 * i4 + 3];
+                continue;
+              }
               // the DS partials added in head-dim order by every wave (its own
               // from registers): identical sums in all of them
               float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
