@@ -395,23 +395,27 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
           for (int i4 = 0; i4 < 4; ++i4)
             x4[(wave * J + j0 + i4) * 64 + lane] = make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
         };
-        auto sum = [&](f32x16& a, int j0) {   // partials added in head-dim order
+        auto sum = [&](f32x16& a, int j0) {
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int pp = 0; pp < DS; ++pp) {
-              const float4 v4 = pp == dh ? make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3])
-                                         : x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
-              if (pp == 0) {
-                t4 = v4;
+            for (int i4 = 0; i4 < 4; ++i4) {
+              float4 t4;
+              if constexpr (DS == 2) {
+                // own + partner: addition commutes, so both waves get the same bits
+                const float4 o4 = x4[((wave ^ 1) * J + j0 + i4) * 64 + lane];
+                t4 = make_float4(a[4 * i4] + o4.x, a[4 * i4 + 1] + o4.y, a[4 * i4 + 2] + o4.z, a[4 * i4 + 3] + o4.w);
               } else {
-                t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
+                // all DS partials, the own one included, read back and added in
+                // head-dim order by every wave
+                t4 = x4[((wave - dh) * J + j0 + i4) * 64 + lane];
+#pragma unroll
+                for (int pp = 1; pp < DS; ++pp) {
+                  const float4 v4 = x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
+                  t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
+                }
               }
+              a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
             }
-            a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
-          }
-        };
+          };
         if constexpr (C::XCH_TWO_PHASE) {
           if (kind != 0) put(s[0], 0);
           block_sync();

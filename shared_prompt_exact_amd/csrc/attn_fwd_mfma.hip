@@ -214,19 +214,13 @@ __global__ void __launch_bounds__(NW * 64)
                 s[kb][4 * i4 + 3] = dh == 0 ? s[kb][4 * i4 + 3] + t.w : t.w + s[kb][4 * i4 + 3];
                 continue;
               }
-              // the DS partials added in head-dim order by every wave (its own
-              // from registers): identical sums in all of them
-              float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+              // the DS partials, this wave's own included, read back and added
+              // in head-dim order by every wave: identical sums in all of them
+              float4 t = x4[((wave - dh) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
 #pragma unroll
-              for (int pp = 0; pp < DS; ++pp) {
-                const float4 v4 = pp == dh ? make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2],
-                                                         s[kb][4 * i4 + 3])
-                                           : x4[((wave - dh + pp) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
-                if (pp == 0) {
-                  t = v4;
-                } else {
-                  t.x += v4.x; t.y += v4.y; t.z += v4.z; t.w += v4.w;
-                }
+              for (int pp = 1; pp < DS; ++pp) {
+                const float4 v4 = x4[((wave - dh + pp) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
+                t.x += v4.x; t.y += v4.y; t.z += v4.z; t.w += v4.w;
               }
               s[kb][4 * i4 + 0] = t.x;
               s[kb][4 * i4 + 1] = t.y;
