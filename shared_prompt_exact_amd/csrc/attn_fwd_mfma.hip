@@ -178,12 +178,37 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
       if (kind != 0) {
+        if constexpr (KTH <= 8) {
+          // the K operands of k-step kk+1 are read before the MFMAs of step
+          // kk (scheduling fences keep them there), so their LDS latency
+          // overlaps MFMA work
+          bf16x8 ka[NB32];
 #pragma unroll
-        for (int kk = 0; kk < KTH; ++kk) {
+          for (int kb = 0; kb < NB32; ++kb) ka[kb] = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
 #pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
-            s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
-          if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          for (int kk = 0; kk < KTH; ++kk) {
+            bf16x8 kn[NB32];
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb) kn[kb] = ka[kb];
+            if (kk + 1 < KTH) {
+#pragma unroll
+              for (int kb = 0; kb < NB32; ++kb) kn[kb] = row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk + 1, hf);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb) s[kb] = mfma32(ka[kb], qB[kk], s[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb) ka[kb] = kn[kb];
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KTH; ++kk) {
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+              s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
+            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       if constexpr (DS > 1) {
@@ -279,12 +304,21 @@ __global__ void __launch_bounds__(NW * 64)
             }
         if constexpr (DBH <= 4) {
           // k-step outer: the DBH accumulators are independent, so
-          // consecutive MFMAs do not wait on each other
+          // consecutive MFMAs do not wait on each other; each V operand is
+          // read one MFMA ahead (scheduling fences hold the order)
+          bf16x8 cur = trans_operand<D>(Vs, 0, dh * DBH * 32, 0, lane);
 #pragma unroll
-          for (int ks = 0; ks < K16; ++ks)
-#pragma unroll
-            for (int db = 0; db < DBH; ++db)
-              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
+          for (int x = 0; x < K16 * DBH; ++x) {
+            const int ks = x / DBH, db = x % DBH;
+            bf16x8 nxt = cur;
+            if (x + 1 < K16 * DBH) {
+              nxt = trans_operand<D>(Vs, 0, (dh * DBH + (x + 1) % DBH) * 32, (x + 1) / DBH, lane);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            acc[db] = mfma32(cur, pB[ks], acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+          }
         } else {
 #pragma unroll
           for (int db = 0; db < DBH; ++db) {
