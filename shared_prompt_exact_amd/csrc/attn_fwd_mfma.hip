@@ -178,10 +178,11 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
       if (kind != 0) {
-        if constexpr (KTH <= 8) {
+        if constexpr (KTH <= 8 && DS != 2) {
           // the K operands of k-step kk+1 are read before the MFMAs of step
           // kk (scheduling fences keep them there), so their LDS latency
-          // overlaps MFMA work
+          // overlaps MFMA work (measured slower with the two-way head-dim
+          // split, which keeps the compiler's order)
           bf16x8 ka[NB32];
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb) ka[kb] = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
@@ -302,7 +303,7 @@ __global__ void __launch_bounds__(NW * 64)
               l += p;
               pB[2 * kb + hs][j] = (__bf16)p;
             }
-        if constexpr (DBH <= 4) {
+        if constexpr (DBH <= 4 && DS != 2) {
           // k-step outer: the DBH accumulators are independent, so
           // consecutive MFMAs do not wait on each other; each V operand is
           // read one MFMA ahead (scheduling fences hold the order)
@@ -319,6 +320,13 @@ __global__ void __launch_bounds__(NW * 64)
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
           }
+        } else if constexpr (DBH <= 4) {
+          // k-step outer, operands read where the compiler places them
+#pragma unroll
+          for (int ks = 0; ks < K16; ++ks)
+#pragma unroll
+            for (int db = 0; db < DBH; ++db)
+              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
         } else {
 #pragma unroll
           for (int db = 0; db < DBH; ++db) {
