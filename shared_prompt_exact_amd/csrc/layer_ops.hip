@@ -172,6 +172,46 @@ __global__ void __launch_bounds__(256)
   p[i + half] = f32_to_bf16(a * s + b * c);
 }
 
+// The same rotation with the angle work shared by the heads: a thread takes
+// token t and the eight pairs (8j + e, 8j + e + D/2), forms their eight
+// angles and sin/cos once (as above), then rotates them in every head with
+// 16-byte loads and stores.  Needs D % 16 == 0 and a 16-byte aligned x.
+__global__ void __launch_bounds__(256)
+    rope_kernel_x8(int64_t n_threads, int H, int D, Groups G, double log2_base, int inverse,
+                 uint16_t* __restrict__ x) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_threads) return;
+  const int half = D / 2, g8 = half / 8;
+  const int j = (int)(idx % g8);
+  const int t = (int)(idx / g8);
+  const int pos = packed_position(G, t);
+  float c[8], s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = 8 * j + e;
+    const double inv_freq = exp2(-(2.0 * i / D) * log2_base);
+    double ang = (double)pos * inv_freq;
+    ang -= 6.283185307179586 * rint(ang / 6.283185307179586);
+    sincosf((float)ang, &s[e], &c[e]);
+    if (inverse) s[e] = -s[e];
+  }
+  uint16_t* row = x + (int64_t)t * H * D + 8 * j;
+  for (int h = 0; h < H; ++h) {
+    uint4* pa = reinterpret_cast<uint4*>(row + (int64_t)h * D);
+    uint4* pb = reinterpret_cast<uint4*>(row + (int64_t)h * D + half);
+    float a[8], b[8], ra[8], rb[8];
+    unpack8(*pa, a);
+    unpack8(*pb, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ra[e] = a[e] * c[e] - b[e] * s[e];
+      rb[e] = a[e] * s[e] + b[e] * c[e];
+    }
+    *pa = pack8(ra);
+    *pb = pack8(rb);
+  }
+}
+
 __device__ __forceinline__ float sigmoid(float u) { return 1.f / (1.f + __expf(-u)); }
 
 // m = silu(u) * g, eight elements per thread.
@@ -241,6 +281,11 @@ hipError_t launch_rmsnorm_bwd(int T, int H, const void* x, const void* w, const 
 hipError_t launch_rope(int T, int H, int D, const Groups& G, float base, int inverse, void* x, hipStream_t s) {
   const int64_t n = (int64_t)T * H * (D / 2);
   if (n == 0) return hipSuccess;
+  if (D % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+    const int64_t n8 = (int64_t)T * (D / 16);
+    return launch("rope", rope_kernel_x8, dim3(blocks256(n8)), dim3(256), 0, s, n8, H, D, G, log2((double)base),
+                  inverse, static_cast<uint16_t*>(x));
+  }
   return launch("rope", rope_kernel, dim3(blocks256(n)), dim3(256), 0, s, n, H, D, G, log2((double)base), inverse,
                 static_cast<uint16_t*>(x));
 }

@@ -78,11 +78,12 @@ def test_rmsnorm():
     tight("dw", host(dw), wdw)
 
 
-def test_rope_logical_positions():
+@pytest.mark.parametrize("head_dim", [64, 24])   # 16-byte vector path; scalar path
+def test_rope_logical_positions(head_dim):
     rng = np.random.default_rng(2)
     groups = [(3, 50, 40), (2, 0, 30), (1, 7, 0)]
     T = sum(P + N * R for N, P, R in groups)
-    x = rounded(rng, T, 2, 64)
+    x = rounded(rng, T, 2, head_dim)
     t = bf(x)
     dk.dualkv_rope(t, groups, 1e4)
     pos = ol.packed_positions(groups)
