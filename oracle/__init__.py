@@ -24,10 +24,12 @@ the oracle is standard attention written out plainly:
 * ``oracle.groups``      several prompt groups in one packed micro-batch;
 * ``oracle.rows``        selected rows of the outputs, for full-size checks;
 * ``oracle.layer``       a pre-norm decoder layer (RMSNorm, RoPE at logical
-                         positions, attention, SwiGLU MLP) on packed rows.
+                         positions, attention, SwiGLU MLP) on packed rows;
+* ``oracle.rounding``    the per-element error envelope of a bf16 backward
+                         (a tolerance model for ill-conditioned inputs).
 
 All floating point is fp64.  Parity of every function is pinned by the
 ``-m "not gpu"`` tests (closed forms, library routines, finite
 differences, sum rules); see ``tests/test_oracle_*.py``.
 """
-from . import mask, dense, replicated, repack, groups, layer  # noqa: F401
+from . import mask, dense, replicated, repack, groups, layer, rounding  # noqa: F401

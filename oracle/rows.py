@@ -11,6 +11,8 @@ the N sequences [prompt; response n]), evaluated only where asked:
   row is seen by every query row whose visible range holds it; each such
   query's softmax statistics (LSE, O, Delta) are computed from its full
   visible key range, in query chunks, so no value comes from elsewhere.
+  Queries that cannot see a wanted key, or whose dO is zero, add nothing
+  and are left out.
 
 Visible key range of a query (logical position p, window W): positions
 [max(0, p-W+1), p] of its sequence; padded rows (r >= L_n) see nothing and
@@ -80,7 +82,21 @@ def query_rows(q, k, v, do, rows, N, P, R, window=0, scale=None, valid_len=None,
 
 def key_rows(q, k, v, do, rows, kv_head, N, P, R, window=0, scale=None, valid_len=None,
              chunk=1024):
-    """Return dict(dk [n,D], dv [n,D]) of packed key rows `rows` of one KV head."""
+    """Return dict(dk [n,D], dv [n,D]) of packed key rows `rows` of one KV head.
+
+    Work is limited to what can reach the wanted keys, which leaves the
+    result unchanged:
+     * per sequence, only queries whose visible range [p-W+1, p] holds one
+       of the wanted key positions;
+     * a query whose dO row (of that head) is all zero adds exactly zero to
+       dK and dV (dp = 0 and Delta = dO . O = 0, so ds = 0), and is skipped;
+     * each chunk of queries scores only the key positions any of them can
+       see, [min p - W + 1, max p]; every query's softmax still covers its
+       whole visible range.
+    The arithmetic is fp64 (torch CPU ops, which use every host thread).
+    """
+    import torch
+
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
@@ -90,61 +106,81 @@ def key_rows(q, k, v, do, rows, kv_head, N, P, R, window=0, scale=None, valid_le
     rows = [int(x) for x in rows]
     dk = np.zeros((len(rows), D))
     dv = np.zeros((len(rows), D))
-    # Queries that can see any of the key rows, grouped by sequence.
-    # Sequence -1 is the prompt (copy 0), n >= 0 the responses.
+    c = kv_head
+
     def seq_of(j):
         return -1 if j < P else (j - P) // R
 
+    # Sequence -1 is the prompt's own queries (copy 0), n >= 0 response n;
+    # every response sees the prompt keys.
     wanted = set(seq_of(j) for j in rows)
     if -1 in wanted:
-        wanted |= set(range(N))          # every response sees the prompt
-    c = kv_head
+        wanted |= set(range(N))
     for seq in sorted(wanted):
         if seq < 0:
-            qrows = np.arange(P)
             seq_rows = np.arange(P)
             nvalid = P
+            qrows_all = np.arange(P)
+            qpos_all = np.arange(P)
+            local = [(a, j) for a, j in enumerate(rows) if j < P]
         else:
-            # queries before the earliest wanted key of this sequence see none
-            # of them (unless prompt keys are wanted: every query sees those)
-            r_first = 0
-            if not any(j < P for j in rows):
-                r_first = min(j - P - seq * R for j in rows if seq_of(j) == seq)
-            qrows = P + seq * R + np.arange(r_first, L[seq])
             seq_rows = np.concatenate([np.arange(P), P + seq * R + np.arange(R)])
             nvalid = P + L[seq]
-        if len(qrows) == 0:
-            continue
-        kk = k[seq_rows, c, :].astype(np.float64)
-        vv = v[seq_rows, c, :].astype(np.float64)
-        # logical positions of this sequence's key rows and of the queries
-        kpos = np.arange(len(seq_rows))
-        qpos = qrows if seq < 0 else P + (qrows - P - seq * R)
-        # which of the wanted key rows live in this sequence, at which index
-        local = [(a, int(np.searchsorted(seq_rows, j))) for a, j in enumerate(rows)
-                 if (j < P) or (seq >= 0 and seq_of(j) == seq)]
+            qrows_all = P + seq * R + np.arange(L[seq])
+            qpos_all = P + np.arange(L[seq])
+            local = [(a, j if j < P else P + (j - P - seq * R)) for a, j in enumerate(rows)
+                     if j < P or seq_of(j) == seq]
+        # wanted keys past the sequence's valid range are seen by nothing
+        local = [(a, kp) for a, kp in local if kp < nvalid]
         if not local:
             continue
-        sel = np.array([li for _, li in local])
+        out_idx = np.array([a for a, _ in local])
+        kps = np.array([kp for _, kp in local])
+        see = np.zeros(len(qpos_all), dtype=bool)
+        for kp in np.unique(kps):                # queries at [kp, kp + W) see key kp
+            band = qpos_all >= kp
+            if window > 0:
+                band &= qpos_all < kp + window
+            see |= band
+        qrows_s, qpos_s = qrows_all[see], qpos_all[see]
+        if len(qrows_s) == 0:
+            continue
+        kk_all = torch.from_numpy(np.ascontiguousarray(k[seq_rows, c, :], dtype=np.float64))
+        vv_all = torch.from_numpy(np.ascontiguousarray(v[seq_rows, c, :], dtype=np.float64))
         for h in range(c * g, (c + 1) * g):
-            for a0 in range(0, len(qrows), chunk):
-                qi = qrows[a0:a0 + chunk]
-                pi = qpos[a0:a0 + chunk]
-                s = scale * (q[qi, h, :].astype(np.float64) @ kk.T)
-                vis = (kpos[None, :] <= pi[:, None]) & (kpos[None, :] < nvalid)
+            live = np.any(do[qrows_s, h, :] != 0, axis=1)
+            qr, qp = qrows_s[live], qpos_s[live]
+            # chunks of at most `chunk` queries inside runs of consecutive
+            # positions (a chunk's key range stays one query's range + chunk)
+            cuts = np.flatnonzero(np.diff(qp) != 1) + 1
+            starts = []
+            for r0, r1 in zip(np.r_[0, cuts], np.r_[cuts, len(qp)]):
+                starts += [(a, min(a + chunk, r1)) for a in range(r0, r1, chunk)]
+            for a0, a1 in starts:
+                qi, pi = qr[a0:a1], qp[a0:a1]
+                lo = max(0, int(pi.min()) - window + 1) if window > 0 else 0
+                hi = int(pi.max()) + 1                       # key positions [lo, hi)
+                kk, vv = kk_all[lo:hi], vv_all[lo:hi]
+                kpos = torch.arange(lo, hi, dtype=torch.int64)
+                pt = torch.from_numpy(pi.astype(np.int64))
+                qq = torch.from_numpy(np.ascontiguousarray(q[qi, h, :], dtype=np.float64))
+                dd = torch.from_numpy(np.ascontiguousarray(do[qi, h, :], dtype=np.float64))
+                s = (qq @ kk.T) * scale
+                vis = (kpos[None, :] <= pt[:, None]) & (kpos[None, :] < nvalid)
                 if window > 0:
-                    vis &= (pi[:, None] - kpos[None, :]) < window
-                s = np.where(vis, s, -np.inf)
-                m = s.max(axis=1)
-                lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-                p = np.exp(s - lse[:, None])
-                o = p @ vv
-                dd = do[qi, h, :].astype(np.float64)
-                delta = (dd * o).sum(axis=1)
-                psel = p[:, sel]
-                dpsel = dd @ vv[sel].T
-                dssel = psel * (dpsel - delta[:, None])
-                qq = q[qi, h, :].astype(np.float64)
-                dk[[a for a, _ in local]] += scale * (dssel.T @ qq)
-                dv[[a for a, _ in local]] += psel.T @ dd
+                    vis &= (pt[:, None] - kpos[None, :]) < window
+                s.masked_fill_(~vis, float("-inf"))
+                m = s.max(dim=1).values
+                s.sub_(m[:, None]).exp_()                    # unnormalised p
+                s.div_(s.sum(dim=1, keepdim=True))           # p
+                o = s @ vv
+                delta = (dd * o).sum(dim=1)
+                inr = (kps >= lo) & (kps < hi)
+                if not inr.any():
+                    continue
+                sel = torch.from_numpy(kps[inr] - lo)
+                psel = s[:, sel]
+                dssel = psel * (dd @ vv[sel].T - delta[:, None])
+                dk[out_idx[inr]] += scale * (dssel.T @ qq).numpy()
+                dv[out_idx[inr]] += (psel.T @ dd).numpy()
     return dict(dk=dk, dv=dv)

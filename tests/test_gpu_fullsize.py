@@ -4,8 +4,12 @@ The oracle cannot afford whole tensors at these sizes, so each case checks
  * sampled query rows (prompt start/middle/end, response starts and ends,
    padded rows): O, LSE and dQ against the oracle's definition of those rows;
  * sampled response key rows of two KV heads: dK, dV;
- * sampled prompt key rows of KV head 0 where the oracle's cost is bounded
-   (every response's queries must be recomputed for them);
+ * sampled prompt key rows (start, middle, around P - W under a window, end):
+   dK, dV summed over the prompt's own queries and every response.  Where
+   the oracle can afford every query head of the group, against the main
+   run; otherwise a second backward with dO kept on one query head only
+   (dO zero elsewhere, so every other head and KV head must come out
+   exactly zero) is checked against the oracle on that same dO;
  * identities over every row: sum_j dK_j = 0 and sum_j dV_j = sum of dO over
    the group's valid query rows, per KV head and dim; <Q,dQ> = <K,dK> and
    <V,dV> = <O,dO>.
@@ -27,7 +31,7 @@ from parity_utils import check, inputs_on_device
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
 
 NAMES = ["qwen3_8b", "dapo_long", "moe_30b", "gemma_global", "gemma_swa"]
-PROMPT_KEY_BUDGET = 6e8      # oracle pairs for sampled prompt keys (one KV head)
+PROMPT_KEY_BUDGET = 2.5e9    # oracle score elements for the prompt-key check (all heads of a group)
 
 
 def log(*a):
@@ -63,6 +67,29 @@ def sample_key_rows(w, L, n):
     return sorted(set(out))
 
 
+def prompt_key_rows(w):
+    P, W = w.prompt_len, w.window
+    cand = {0, 1, P // 2, P - 64, P - 2, P - 1}
+    if W > 0:
+        cand |= {P - W - 1, P - W, P - W + 1, P - W // 2}
+    return sorted(j for j in cand if 0 <= j < P)
+
+
+def score_elements(w, L, keys):
+    """(query, key) scores the row oracle evaluates for prompt key rows
+    `keys`, per query head: each query that sees one of them scores its
+    whole visible range."""
+    P, W = w.prompt_len, w.window
+    pos = np.arange(P + max(L, default=0))
+    see = np.zeros(len(pos), dtype=bool)
+    for kp in keys:
+        see |= (pos >= kp) & ((pos < kp + W) if W > 0 else True)
+    span = np.minimum(pos + 1, W) if W > 0 else pos + 1
+    prompt = int(span[:P][see[:P]].sum())
+    resp = sum(int(span[P:P + l][see[P:P + l]].sum()) for l in L)
+    return prompt + resp
+
+
 def dot64(a, b, rows=4096):
     """sum(a * b) in fp64, in row chunks (a, b: float32 arrays)."""
     t = 0.0
@@ -88,9 +115,8 @@ def test_full_size_layer(name):
     o, lse = dk.dualkv_fwd(d["q"], d["k"], d["v"], N, P, R, **kw)
     dq, dkk, dv = dk.dualkv_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], N, P, R, **kw)
     torch.cuda.synchronize()
-    del d
     O, LSE, DQ, DK, DV = (host32(t) for t in (o, lse, dq, dkk, dv))
-    del o, lse, dq, dkk, dv
+    del dq, dkk, dv
     torch.cuda.empty_cache()
 
     # sampled query rows
@@ -109,18 +135,44 @@ def test_full_size_layer(name):
         for nm, got, want in (("dk", DK[kr, c], ref["dk"]), ("dv", DV[kr, c], ref["dv"])):
             log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False))
 
-    # sampled prompt key rows where affordable
-    pairs = P * (P + sum(L))
-    if P and w.window <= 0 and pairs <= PROMPT_KEY_BUDGET:
-        pk = sorted({0, P // 2, P - 1})
-        log(f"{name}: oracle on prompt key rows {pk}, KV head 0")
-        ref = orows.key_rows(x.q, x.k, x.v, x.do, pk, 0, N, P, R, w.window, None, x.valid_len)
-        for nm, got, want in (("dk", DK[pk, 0], ref["dk"]), ("dv", DV[pk, 0], ref["dv"])):
-            log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False))
+    # sampled prompt key rows: the sum over the prompt's queries and all N
+    # responses
+    pk = prompt_key_rows(w)
+    g = w.n_q_heads // w.n_kv_heads
+    if pk:
+        cost = score_elements(w, L, pk)
+        if cost * g <= PROMPT_KEY_BUDGET:
+            c = w.n_kv_heads - 1
+            log(f"{name}: oracle on prompt key rows {pk}, KV head {c}, all {g} query heads ({cost * g:.2e} scores)")
+            ref = orows.key_rows(x.q, x.k, x.v, x.do, pk, c, N, P, R, w.window, None, x.valid_len)
+            for nm, got, want in (("dk", DK[pk, c], ref["dk"]), ("dv", DV[pk, c], ref["dv"])):
+                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False))
+        else:
+            h1 = w.n_q_heads - 1
+            c = h1 // g
+            log(f"{name}: backward with dO on query head {h1} only")
+            do1 = torch.zeros_like(d["do"])
+            do1[:, h1] = d["do"][:, h1]
+            dq1, dk1, dv1 = dk.dualkv_bwd(d["q"], d["k"], d["v"], o, lse, do1, N, P, R, **kw)
+            torch.cuda.synchronize()
+            others = [h for h in range(w.n_q_heads) if h != h1]
+            assert bool((dq1[:, others] == 0).all()), "dQ of heads without dO must be exactly 0"
+            assert bool((dk1[:, :c] == 0).all()) and bool((dv1[:, :c] == 0).all()), \
+                "dK/dV of KV heads without dO must be exactly 0"
+            DK1, DV1 = host32(dk1[pk, c]), host32(dv1[pk, c])
+            del do1, dq1, dk1, dv1
+            xdo = np.zeros_like(x.do)
+            xdo[:, h1] = x.do[:, h1]
+            log(f"{name}: oracle on prompt key rows {pk}, KV head {c}, query head {h1} ({cost:.2e} scores)")
+            ref = orows.key_rows(x.q, x.k, x.v, xdo, pk, c, N, P, R, w.window, None, x.valid_len)
+            del xdo
+            for nm, got, want in (("dk", DK1, ref["dk"]), ("dv", DV1, ref["dv"])):
+                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False))
+    del d, o, lse
+    torch.cuda.empty_cache()
 
     # identities over all rows (fp64 sums of the GPU outputs)
     log(f"{name}: identities")
-    g = w.n_q_heads // w.n_kv_heads
     T = P + N * R
     live = np.isfinite(LSE)                                  # [Hq, T]
     for c in range(w.n_kv_heads):

@@ -10,16 +10,16 @@ import torch
 
 import shared_prompt_exact_amd as dk
 import workloads
-from oracle import replicated
+from oracle import replicated, rounding
 
-from parity_utils import check, host, inputs_on_device
+from parity_utils import STRESS, check, host, inputs_on_device, stress_modifier
 
 pytestmark = pytest.mark.gpu
 
 W = workloads.Workload
 
 
-def run_case(w, impl=dk.IMPL_AUTO, backward=True, modify=None, delta_o=None, bwd_elementwise=True):
+def run_case(w, impl=dk.IMPL_AUTO, backward=True, modify=None, delta_o=None, envelope=None):
     print(f"case {w}", flush=True)
     x = workloads.generate(w)
     if modify is not None:
@@ -39,7 +39,8 @@ def run_case(w, impl=dk.IMPL_AUTO, backward=True, modify=None, delta_o=None, bwd
            "lse": check("lse", host(lse), ref["lse"], w.dtype, uv)}
     if backward:
         for name, g in zip(("dq", "dk", "dv"), grads):
-            out[name] = check(name, host(g), ref[name], w.dtype, uv, bwd_elementwise)
+            out[name] = check(name, host(g), ref[name], w.dtype, uv,
+                              envelope=None if envelope is None else envelope[name])
     print({k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in out.items()}, flush=True)
     return o, lse, grads
 
@@ -126,43 +127,21 @@ def test_prompt_rows_invariant_to_responses():
     assert torch.equal(l1[:, :P], l2[:, :P])
 
 
-# Online-softmax stress (correctness only): a peaked softmax, and one key
-# that dominates every later query of its sequence, either met first (a
-# prompt key: the running max is set early) or last (a key of the query's
-# own response, met after every prompt tile: the running sum is rescaled
-# late).  All modified values are exact in bf16.  With a near one-hot
-# softmax, dS = P (dP - Delta) cancels, and the backward takes Delta =
-# rowsum(dO * O) from the bf16 O the forward returned: that rounding alone
-# moves dQ by about 9% (rel-L2) on the early-max input (fp64 emulation of
-# exactly that rounding).  So the backward here is compared with the
-# oracle's backward evaluated at its own O rounded to bf16 (the forward's
-# output contract); the forward is compared with the exact oracle (the two
-# oracles agree on it bit for bit) under the full gates.  The backward keeps
-# the rel-L2 gate only: the kernel's O differs from the oracle's in its last
-# bf16 bit where P was rounded before PV, and the same cancellation turns
-# that into dQ errors of 0.2-0.4 of max(RMS, |dQ|) on single elements
-# (emulated in fp64), at a rel-L2 of a few 1e-3.
-STRESS = W("stress", "bf16", 3, 150, 120, 4, 2, 128, 0, seed=41, value_scale=1.0)
-
-
-def _peaked(w, x):
-    x.q *= 4.0
-
-
-def _dominant_key(rows):
-    def modify(w, x):
-        x.q[:, :, 0] = 3.0
-        for j in rows(w):
-            x.k[j, :, 0] = 40.0
-    return modify
-
-
+# Online-softmax stress (parity_utils.STRESS).  With a near one-hot softmax,
+# dS = P (dP - Delta) cancels, and the backward takes Delta = rowsum(dO * O)
+# from the bf16 O the forward returned: that rounding alone moves dQ by
+# about 9% (rel-L2) on the early-max input.  So the backward is compared
+# with the oracle's backward evaluated at its own O rounded to bf16 (the
+# forward's output contract), under the rel-L2 gate and an elementwise gate
+# widened by the rounding envelope of oracle.rounding (the kernel's own
+# bf16 roundings of P, O and dS propagated through the fp64 oracle's
+# quantities); the forward is compared with the exact oracle under the full
+# gates.
 @pytest.mark.parametrize("kind", ["peaked", "early_max", "late_max"])
 def test_online_softmax_stress(kind):
-    P, R = STRESS.prompt_len, STRESS.resp_len
-    modify = {
-        "peaked": _peaked,
-        "early_max": _dominant_key(lambda w: [3]),
-        "late_max": _dominant_key(lambda w: [P + n * R + 70 for n in range(w.n_resp)]),
-    }[kind]
-    run_case(STRESS, modify=modify, delta_o="bf16", bwd_elementwise=False)
+    w = STRESS
+    modify = stress_modifier(kind)
+    x = workloads.generate(w)
+    modify(w, x)
+    env = rounding.backward_envelope(x.q, x.k, x.v, x.do, w.n_resp, w.prompt_len, w.resp_len)
+    run_case(w, modify=modify, delta_o="bf16", envelope=env)

@@ -5,16 +5,24 @@
    computations that share only the token-wise formulas;
  * finite differences of <Y, dY> for dX (prompt and response rows) and for
    one entry of every weight;
+ * RoPE and SiLU: hand-worked values (tests/golden/rope_silu_example.json)
+   that fix the frequency exponent, the (i, i + D/2) pairing and the sense
+   of rotation;
  * RoPE: position 0 is the identity, the inverse undoes it, pair norms are
    kept, and rotated scores depend only on the difference of positions;
  * RMSNorm: invariant to scaling a row (eps -> 0); a constant row maps to
    the weights;
  * SwiGLU backward against finite differences.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
 from oracle import layer as ol
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rope_silu_example.json")
 
 Hq, Hkv, D, Hm, F = 4, 2, 8, 16, 24
 
@@ -117,3 +125,39 @@ def test_swiglu_backward_by_finite_differences():
     fg = ((ol.silu(u) * (g + e) - ol.silu(u) * (g - e)) / (2 * e)) * dm
     np.testing.assert_allclose(du, fu, atol=1e-8)
     np.testing.assert_allclose(dg, fg, atol=1e-8)
+
+
+def test_rope_and_silu_golden_values():
+    with open(GOLDEN) as fh:
+        g = json.load(fh)
+    for case in g["rope"]:
+        x = np.asarray(case["x"], dtype=np.float64)[None]          # [1, H, D]
+        y = ol.rope(x, [case["pos"]], case["base"])
+        np.testing.assert_allclose(y[0], np.asarray(case["y"]), rtol=0, atol=1e-14)
+    u = np.asarray(g["silu"]["u"])
+    np.testing.assert_allclose(ol.silu(u), np.asarray(g["silu"]["y"]), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("mistake", ["interleaved", "exponent", "sense"])
+def test_rope_golden_catches_planted_mistakes(mistake):
+    """Each plausible misreading of the rotation, planted in a copy of the
+    oracle's formula, misses the golden values."""
+    with open(GOLDEN) as fh:
+        case = json.load(fh)["rope"][0]
+    x = np.asarray(case["x"], dtype=np.float64)
+    D = x.shape[1]
+    half = D // 2
+    i = np.arange(half)
+    inv = case["base"] ** (-(i if mistake == "exponent" else 2.0 * i) / D)
+    ang = case["pos"] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    if mistake == "sense":
+        s = -s
+    if mistake == "interleaved":
+        a, b = x[:, 0::2], x[:, 1::2]
+        y = np.empty_like(x)
+        y[:, 0::2], y[:, 1::2] = a * c - b * s, a * s + b * c
+    else:
+        a, b = x[:, :half], x[:, half:]
+        y = np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+    assert np.abs(y - np.asarray(case["y"])).max() > 1e-3
