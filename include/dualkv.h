@@ -53,7 +53,8 @@ enum {
   DUALKV_ERR_INVALID_ARGUMENT = 1,
   DUALKV_ERR_UNSUPPORTED = 2,
   DUALKV_ERR_WORKSPACE_TOO_SMALL = 3,
-  DUALKV_ERR_HIP = 4
+  DUALKV_ERR_HIP = 4,
+  DUALKV_ERR_SCRATCH_LIMIT = 5   /* dualkv_bwd_noalloc: workspace need above its static buffer */
 };
 
 enum { DUALKV_F32 = 0, DUALKV_BF16 = 1 };        /* dualkv_params.dtype */
@@ -126,6 +127,27 @@ int dualkv_bwd(const dualkv_params* p, const void* q, const void* k,
                const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dualkv_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, contract and results as dualkv_bwd, with the
+ * workspace taken from a static device buffer of
+ * DUALKV_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing.
+ * It runs on the current device (the device of `stream`).  Returns
+ * DUALKV_ERR_SCRATCH_LIMIT, launching nothing, when
+ * dualkv_bwd_workspace_bytes(p) exceeds the buffer (the Qwen3-8B-shaped
+ * layer, N=32, P=8192, R=1024, 32/8 heads, D=128, needs about 179 MB).
+ * All calls on one GPU share its buffer: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.
+ */
+#define DUALKV_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int dualkv_bwd_noalloc(const dualkv_params* p, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv,
+                       void* stream);
 
 /*
  * Several prompt groups in one call ("DualKV: Shared-Prompt Flash

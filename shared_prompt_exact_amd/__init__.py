@@ -85,6 +85,8 @@ def load_library():
     lib.dualkv_bwd_workspace_bytes.restype = sz
     lib.dualkv_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dualkv_bwd.restype = ctypes.c_int
+    lib.dualkv_bwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dualkv_bwd_noalloc.restype = ctypes.c_int
     gp = ctypes.POINTER(Group)
     lib.dualkv_repack_groups.argtypes = [vp, vp, i64, gp, i32, i32, vp]
     lib.dualkv_repack_groups.restype = ctypes.c_int
@@ -235,6 +237,28 @@ def dualkv_bwd(q, k, v, o, lse, dout, n_resp, prompt_len, resp_len, window=0, so
     _check(lib.dualkv_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream()),
            "dualkv_bwd")
+    return dq, dk, dv
+
+
+def dualkv_bwd_noalloc(q, k, v, o, lse, dout, n_resp, prompt_len, resp_len, window=0, softmax_scale=0.0,
+                       valid_len=None, impl=IMPL_AUTO, dq=None, dk=None, dv=None):
+    """dualkv_bwd with the library's static per-device workspace (the call
+    allocates nothing on the device; pass dq, dk, dv to allocate nothing
+    here either).  Returns (dq, dk, dv)."""
+    lib = load_library()
+    p = make_params(q, k, n_resp, prompt_len, resp_len, window, softmax_scale, valid_len, impl)
+    _require(v, "v", dtype=q.dtype, shape=k.shape)
+    _require(o, "o", dtype=q.dtype, shape=q.shape)
+    _require(dout, "dout", dtype=q.dtype, shape=q.shape)
+    _require(lse, "lse", dtype=torch.float32, shape=(q.shape[1], q.shape[0]))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, name, dtype=ref.dtype, shape=ref.shape)
+    _check(lib.dualkv_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _stream()),
+           "dualkv_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -3,6 +3,8 @@
 // include/dualkv.h for the contract of every entry point.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace dualkv;
@@ -124,6 +126,8 @@ const char* dualkv_strerror(int status) {
     case DUALKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case DUALKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case DUALKV_ERR_HIP: return "HIP runtime error";
+    case DUALKV_ERR_SCRATCH_LIMIT:
+      return "problem needs more backward workspace than the static scratch buffer of dualkv_bwd_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -234,3 +238,61 @@ int dualkv_bwd(const dualkv_params* p, const void* q, const void* k, const void*
 }
 
 }  // extern "C"
+
+// ---- backward without a caller workspace ---------------------------------
+//
+// The workspace of dualkv_bwd_noalloc is one static device array per GPU
+// (this file's code object is loaded once per device, each with its own
+// copy at its own address).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is passed to
+// kernels.  Every call on a device shares the device's array and leaves its
+// contents behind; the backward writes every workspace element it reads
+// before reading it, so nothing has to start at zero.  Calls that overlap
+// on one device (different streams or threads) race on the array.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[DUALKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DUALKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DUALKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return DUALKV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DUALKV_OK;
+}
+
+}  // namespace
+
+extern "C" int dualkv_bwd_noalloc(const dualkv_params* p, const void* q, const void* k, const void* v,
+                                  const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, void* stream) {
+  const dualkv_group g = group_of_params(p);
+  Problem pr;
+  Groups G;
+  int st = validate(p, &g, 1, &pr, &G);
+  if (st != DUALKV_OK) return st;
+  const int which = choose_bwd(p, pr, G);
+  if (which < 0) return DUALKV_ERR_UNSUPPORTED;
+  if (pr.Tld == 0) return DUALKV_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return DUALKV_ERR_INVALID_ARGUMENT;
+  const size_t need = which == 1 ? bwd_mfma_workspace_bytes(pr, G) : scalar_workspace(pr);
+  if (need > DUALKV_NOALLOC_SCRATCH_BYTES) return DUALKV_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != DUALKV_OK) return st;
+  return dualkv_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, ws, DUALKV_NOALLOC_SCRATCH_BYTES, stream);
+}
