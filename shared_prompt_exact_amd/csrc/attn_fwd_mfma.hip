@@ -378,6 +378,265 @@ __global__ void __launch_bounds__(NW * 64)
   }
 }
 
+// The forward above for head dims a wave holds whole (D <= 128), with
+// cheaper addressing: K tiles in NS slots, then V tiles in NS slots, in a
+// statically sized LDS block, so one base register per row pattern reaches
+// every slot by an immediate offset and every 16-byte chunk by one XOR
+// (lds_tiles.h); tiles are loaded with a scalar tile address plus per-lane
+// offsets fixed for the kernel (rows clamped only on a partial tile).  Same
+// schedule and arithmetic as fwd_mfma_kernel with DS = 1.
+template <int D, int BN, int NW, int NS>
+struct LeanCfg {
+  static constexpr int TILE_BYTES = BN * D * 2;     // one K (or V) tile
+  static constexpr int V_REGION = NS * TILE_BYTES;  // V slots start here
+  static constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
+  static constexpr int KBLK = TILE_BYTES / 1024;    // 1 KiB blocks per tile
+  static constexpr int BPW = KBLK / NW;             // blocks per wave per tile (K and V each)
+  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
+  static_assert(V_REGION + (NS - 1) * TILE_BYTES <= 65536 + V_REGION, "immediate offsets reach every slot");
+};
+
+template <int D, int BN, int NW, int NS>
+__global__ void __launch_bounds__(NW * 64)
+    fwd_lean_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
+                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    uint16_t* __restrict__ o, float* __restrict__ lse) {
+  using C = LeanCfg<D, BN, NW, NS>;
+  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BM = 32 * NW / HG;
+  const int NB = GB.off[G.n];
+  const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
+  if (L < 0) return;
+  const int hgi = L / NB;
+  const int gi = group_of(GB.off, G.n, L % NB);
+  const int blk = L % NB - GB.off[gi];
+  const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    o += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    lse += r0;
+  }
+  const int gpw = pr.g / HG;
+  const int c = hgi / gpw;
+  const int h = c * pr.g + (hgi % gpw) * HG + wave % HG;
+  const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
+
+  const int wr0 = b.r0 + (wave / HG) * 32;
+  const int my_r = wr0 + l32;
+  const bool qvalid = my_r < b.nvalid;
+  const int qpos = b.posoff + my_r;
+  const int64_t qrow = (int64_t)b.base + my_r;
+  const int64_t ostride = (int64_t)pr.Hq * D;
+  const int blk_hi = min(b.r0 + BM, b.nvalid) - 1;
+  const int w_hi = min(wr0 + 31, b.nvalid - 1);
+  const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
+  const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
+
+  bf16x8 qB[KT];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk) {
+    uint4 z = {0, 0, 0, 0};
+    if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf);
+    qB[kk] = __builtin_bit_cast(bf16x8, z);
+  }
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
+
+  // operand bases (bytes from the start of LDS)
+  unsigned kbase = row_base<D>(l32, hf);                 // K row operands, rows l32 (+32 kb)
+  unsigned vb0, vb1;
+  trans_bases<D>(lane, vb0, vb1);                         // V transposed operands
+  vb0 += C::V_REGION;
+  vb1 += C::V_REGION;
+
+  if (blk_hi >= b.r0) {
+    const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
+    const int ntiles = tr.nA + tr.nB;
+    const int64_t rs = (int64_t)pr.Hkv * D;
+    const unsigned row_bytes = (unsigned)(rs * 2);
+    unsigned voff[C::BPW];
+#pragma unroll
+    for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::BPW + j, lane, row_bytes);
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    auto issue = [&](int t) {
+      const KeyTile kt = tile_at(pr, b, tr, t, BN);
+      const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
+      const unsigned kdst = lds0 + (unsigned)((t % NS) * C::TILE_BYTES + wave * C::BPW * 1024);
+      const unsigned vdst = kdst + C::V_REGION;
+      const uint16_t* kg = k + off;
+      const uint16_t* vg = v + off;
+      if (kt.lim >= BN) {
+#pragma unroll
+        for (int j = 0; j < C::BPW; ++j) {
+          dma_block(kg, voff[j], kdst + j * 1024);
+          dma_block(vg, voff[j], vdst + j * 1024);
+        }
+      } else {
+        // partial tile: rows past the last valid one re-read it (finite, masked)
+        constexpr int CPR = D / 8, RPB = 64 / CPR;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
+#pragma unroll
+        for (int j = 0; j < C::BPW; ++j) {
+          const int row = (wave * C::BPW + j) * RPB + ln / CPR;
+          const int src = min(row, kt.lim - 1);
+          const unsigned vo = (unsigned)src * row_bytes + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
+          dma_block(kg, vo, kdst + j * 1024);
+          dma_block(vg, vo, vdst + j * 1024);
+        }
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < ntiles) issue(t);
+
+    auto step = [&](int it, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      constexpr unsigned KIMM = SLOT * C::TILE_BYTES, VIMM = SLOT * C::TILE_BYTES;
+      if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
+      else wait_vmcnt<0>();
+      block_sync();
+      if (it + NS - 1 < ntiles) issue(it + NS - 1);
+      // opaque to the compiler: the per-chunk XORs are recomputed per tile
+      // instead of being hoisted out of the loop into a dozen registers
+      asm volatile("" : "+v"(kbase), "+v"(vb0), "+v"(vb1));
+
+      const KeyTile kt = tile_at(pr, b, tr, it, BN);
+      const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
+      f32x16 s[NB32];
+#pragma unroll
+      for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+      if (kind != 0) {
+        // the K operands of k-step kk+1 are read before the MFMAs of step kk
+        bf16x8 ka[NB32];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb) ka[kb] = row_operand_x<D>(lds, kbase, 0, KIMM + kb * 32 * 2 * D);
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+          bf16x8 kn[NB32];
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb) kn[kb] = ka[kb];
+          if (kk + 1 < KT) {
+#pragma unroll
+            for (int kb = 0; kb < NB32; ++kb)
+              kn[kb] = row_operand_x<D>(lds, kbase, kk + 1, KIMM + kb * 32 * 2 * D);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb) s[kb] = mfma32(ka[kb], qB[kk], s[kb]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb) ka[kb] = kn[kb];
+        }
+        if (kind == 2) {
+          int d0 = qpos - kt.pos0 - 4 * hf;
+          int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
+          asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
+#pragma unroll
+          for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
+              const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+              s[kb][i] = vis ? s[kb][i] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const bool grow = mx * c2 > m + kRescale;
+        if (__any(grow)) {
+          const float mnew = grow ? mx * c2 : m;
+          const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+          m = mnew;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
+        const float muse = m == -INFINITY ? 0.f : m;
+        bf16x8 pB[K16];
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + j], c2, -muse));
+              l += p;
+              pB[2 * kb + hs][j] = (__bf16)p;
+            }
+        // k-step outer over the DB independent accumulators; each V operand
+        // read one MFMA ahead (scheduling fences hold the order)
+        bf16x8 cur = trans_operand_x<D>(lds, vb0, vb1, 0, 0, VIMM);
+#pragma unroll
+        for (int x = 0; x < K16 * DB; ++x) {
+          const int ks = x / DB, db = x % DB;
+          bf16x8 nxt = cur;
+          if (x + 1 < K16 * DB) {
+            nxt = trans_operand_x<D>(lds, vb0, vb1, (x + 1) % DB, (x + 1) / DB, VIMM);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          acc[db] = mfma32(cur, pB[ks], acc[db]);
+          __builtin_amdgcn_sched_barrier(0);
+          cur = nxt;
+        }
+      }
+    };
+    static_assert(NS == 3, "ring of three, unrolled by three");
+    int it = 0;
+    for (; it + NS <= ntiles; it += NS) {
+      step(it, IntC<0>{});
+      step(it + 1, IntC<1>{});
+      step(it + 2, IntC<2>{});
+    }
+    if (it < ntiles) step(it, IntC<0>{});
+    if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+  }
+
+  const float lt = l + swap_halves(l);
+  const bool has = qvalid && lt > 0.f;
+  const float inv = has ? 1.f / lt : 0.f;
+  if (my_r < b.seglen) {
+    uint16_t* orow = o + qrow * ostride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hf;
+        union { __bf16 h[4]; uint2 u; } pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = pk.u;
+      }
+    if (hf == 0)
+      lse[(int64_t)h * pr.Tld + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 struct FwdPlan {
   int NW, BN, DS, HG, BM;
   GroupBlocks gb;
@@ -408,6 +667,15 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
   return p;
 }
 
+template <int D, int BN, int NW, int NS>
+hipError_t run_lean(const Problem& pr, const Groups& G, const FwdPlan& p, const void* q, const void* k,
+                    const void* v, void* o, float* lse, hipStream_t stream) {
+  static_assert(LeanCfg<D, BN, NW, NS>::LDS_BYTES <= 160 * 1024, "LDS budget");
+  return launch("fwd", fwd_lean_kernel<D, BN, NW, NS>, dim3((unsigned)p.nwg), dim3(NW * 64), 0, stream, pr, G,
+                p.gb, p.HG, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse);
+}
+
 template <int D, int BN, int NW, int NS, int DS>
 hipError_t run(const Problem& pr, const Groups& G, const FwdPlan& p, const void* q, const void* k, const void* v,
                void* o, float* lse, hipStream_t stream) {
@@ -434,8 +702,8 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   const FwdPlan p = plan(pr, G);
   if (p.nwg == 0) return hipSuccess;
   switch (pr.D) {
-    case 64: return run<64, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
-    case 128: return run<128, 64, 8, 3, 1>(pr, G, p, q, k, v, o, lse, stream);
+    case 64: return run_lean<64, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
+    case 128: return run_lean<128, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 256: return run<256, 32, 8, 3, 2>(pr, G, p, q, k, v, o, lse, stream);
     case 512: return run<512, 32, 8, 2, 4>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;

@@ -116,4 +116,81 @@ __device__ __forceinline__ bf16x8 trans_operand(const uint16_t* tile, int row0, 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// ---- XOR-addressed operand reads -------------------------------------------
+//
+// In a swizzled tile the byte address of (row, chunk c) is
+//   row * 2D + ((c ^ swz(row)) << 4),
+// and since row * 2D has no bits inside the chunk field (bits 4 .. 4 +
+// log2(D/8) - 1), that is  (row * 2D + (swz(row) << 4)) ^ (c << 4).  So a
+// lane keeps ONE base address per row pattern and reaches every chunk with a
+// single v_xor against a compile-time constant; tile, slot and 16-row steps
+// (which leave swz unchanged) are immediate offsets of the LDS instruction.
+// `base` values below are byte offsets from the start of LDS.
+
+__device__ __forceinline__ const uint16_t* lds_at(const uint16_t* lds0, unsigned byte_off) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(lds0) + byte_off);
+}
+
+// Base of the row operand for this lane: row `row`, wave half hf folded in
+// (logical chunk 2*kk + hf is then base ^ (kk << 5)).
+template <int D>
+__device__ __forceinline__ unsigned row_base(int row, int hf) {
+  return (unsigned)row * (2 * D) + (unsigned)((swz<D>(row) ^ hf) << 4);
+}
+
+// Row operand of k-step kk from a row base, at byte offset `imm` (tile/slot).
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand_x(const uint16_t* lds0, unsigned base, int kk, unsigned imm) {
+  return *reinterpret_cast<const bf16x8*>(lds_at(lds0, (base ^ ((unsigned)kk << 5)) + imm));
+}
+
+// Bases of the transposed operand (see trans_operand): the lane's first
+// and second 8-row reads, column block 0, k-step 0.
+template <int D>
+__device__ __forceinline__ void trans_bases(int lane, unsigned& b0, unsigned& b1) {
+  const int g = lane >> 4, s = lane & 15;
+  const int hf = g >> 1, ib = (g & 1) * 16;
+  const int col = ib + 4 * (s & 3);                  // 0 .. 31
+  const int r0 = 4 * hf + (s >> 2);                  // 0 .. 7
+  b0 = (unsigned)r0 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r0))) << 4) + (unsigned)((col & 7) * 2);
+  const int r1 = r0 + 8;
+  b1 = (unsigned)r1 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r1))) << 4) + (unsigned)((col & 7) * 2);
+}
+
+// Transposed operand of column block cb (32 columns) and k-step ks from the
+// bases above, at byte offset `imm`: 32-column blocks are chunk groups of 4,
+// i.e. an XOR of (4*cb) << 4 = cb << 6; k-steps are 16 rows (an immediate).
+template <int D>
+__device__ __forceinline__ bf16x8 trans_operand_x(const uint16_t* lds0, unsigned b0, unsigned b1, int cb, int ks,
+                                                  unsigned imm) {
+  const unsigned x = (unsigned)cb << 6;
+  const unsigned off = imm + (unsigned)ks * 16u * (2 * D);
+  const lds_short4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_as3*)lds_at(lds0, (b0 ^ x) + off));
+  const lds_short4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_as3*)lds_at(lds0, (b1 ^ x) + off));
+  const u32x2 xa = __builtin_bit_cast(u32x2, a), yb = __builtin_bit_cast(u32x2, b);
+  const uint4 u = {xa.x, xa.y, yb.x, yb.y};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Per-lane global offset (bytes) of this lane's chunk in 1 KiB block `blk`
+// of a tile whose rows are `row_bytes` apart: the lane lands at physical
+// chunk lane % (D/8) of its row, so it fetches logical chunk
+// (lane % (D/8)) ^ swz(row).  Valid for every tile of full rows.
+template <int D>
+__device__ __forceinline__ unsigned dma_lane_offset(int blk, int lane, unsigned row_bytes) {
+  constexpr int CPR = D / 8, RPB = 64 / CPR;
+  const int row = blk * RPB + lane / CPR;
+  const int c = (lane % CPR) ^ swz<D>(row);
+  return (unsigned)row * row_bytes + (unsigned)c * 16u;
+}
+
+// One 1 KiB block of a tile by direct global->LDS load: global address
+// `gbase` (wave-uniform, scalar) + this lane's offset, LDS destination
+// `lds_byte` (wave-uniform).  No vector arithmetic on the address.
+__device__ __forceinline__ void dma_block(const void* gbase, unsigned voff, unsigned lds_byte) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds_byte));
+}
+
 }  // namespace dualkv
