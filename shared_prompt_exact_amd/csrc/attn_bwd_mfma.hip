@@ -543,6 +543,333 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   }
 }
 
+// The dK/dV kernel above for head dim 128 (a wave holds whole rows, one
+// 32-key tile per wave, V in LDS), with cheaper addressing: a statically
+// sized LDS block (V tile, then NS query stages), operand addresses derived
+// from a few per-lane bases with one XOR per 16-byte chunk and immediate
+// tile offsets (lds_tiles.h), and stage loads from a scalar row address
+// plus one per-lane offset fixed for the kernel (rows clamped only on a
+// partial stage).  Same work items, schedule and arithmetic.
+template <int D, int NWK, int NS>
+__global__ void __launch_bounds__(NWK * 64)
+    bwd_dkdv_lean_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
+                         const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                         const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
+                         const float* __restrict__ delta, uint16_t* __restrict__ dk,
+                         uint16_t* __restrict__ dv, float* __restrict__ part_k,
+                         float* __restrict__ part_v) {
+  using C = KvCfg<D, NWK, NS, 1, false, 1>;
+  constexpr int KT = D / 16, DB = D / 32, BK = C::BK;
+  constexpr unsigned V_BYTES = C::V_ELEMS * 2, Q_BYTES = C::Q_ELEMS * 2, DO_BYTES = C::DO_ELEMS * 2;
+  constexpr unsigned STAGE_BYTES = C::STAGE * 2;
+  static_assert(C::SBPW == 2 && C::QBLK == NWK, "one Q block and one dO block per wave and stage");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- decode the work item (groups in order, longest first within a
+  // group and KV head)
+  const int per_head = KG.off[G.n];
+  const int Lid = balanced_block(blockIdx.x, pa.Hkv, per_head);
+  if (Lid < 0) return;                        // grid padding (whole workgroup)
+  KvItem it;
+  it.c = Lid / per_head;
+  int x = Lid % per_head;
+  const int gi = group_of(KG.off, G.n, x);
+  x -= KG.off[gi];
+  const Problem pr = group_problem(pa, G, gi);
+  const KvShape sh = KG.sh[gi];
+  {
+    const int64_t r0 = G.row0[gi];
+    q += r0 * pr.Hq * D;
+    dout += r0 * pr.Hq * D;
+    k += r0 * pr.Hkv * D;
+    v += r0 * pr.Hkv * D;
+    dk += r0 * pr.Hkv * D;
+    dv += r0 * pr.Hkv * D;
+    lse2 += r0;
+    delta += r0;
+    part_k += KG.part[gi];
+    part_v += KG.part[gi];
+  }
+  // response slots exist only for prompt tiles t0 .. nPt-1 (all of them
+  // without a window)
+  const int nPtR = sh.nPt - sh.t0;
+  if (x < nPtR * (sh.slots - 1) + sh.nPt) {
+    it.seg = -1;
+    if (x < nPtR * (sh.slots - 1)) {                      // response slots first
+      it.slot = 1 + x / nPtR;
+      it.k0 = (sh.t0 + x % nPtR) * BK;
+    } else {                                              // then the prompt slot
+      it.slot = 0;
+      it.k0 = (x - nPtR * (sh.slots - 1)) * BK;
+    }
+  } else {
+    x -= nPtR * (sh.slots - 1) + sh.nPt;
+    it.seg = x % pr.N;
+    it.k0 = (x / pr.N) * BK;
+    it.slot = 0;
+  }
+  const int c = it.c;
+  const int seg_base = it.seg < 0 ? 0 : pr.P + it.seg * pr.R;
+  const int seg_valid = it.seg < 0 ? pr.P : resp_valid(pr, it.seg);
+  const int seg_len = it.seg < 0 ? pr.P : pr.R;
+  const int posoff = it.seg < 0 ? 0 : pr.P;
+  const int klim = seg_valid - it.k0;                 // valid keys of the tile
+  const int kp_lo = posoff + it.k0;
+  const int kp_hi = posoff + it.k0 + min(BK, max(klim, 1)) - 1;
+
+  // ---- this wave's 32 keys: K^T as B operands in registers; the V tile
+  // row-major in LDS (B operand of dP)
+  const int wk0 = 32 * wave;                          // first key of the wave in the tile
+  const int my_k = wk0 + l32;
+  const bool kvalid = my_k < klim;
+  const int kpos = kp_lo + my_k;
+  const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
+  const int64_t kstride = (int64_t)pr.Hkv * D;
+  bf16x8 kB[KT];
+#pragma unroll
+  for (int kk = 0; kk < KT; ++kk) {
+    uint4 z = {0, 0, 0, 0};
+    if (kvalid) z = *reinterpret_cast<const uint4*>(k + krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf);
+    kB[kk] = __builtin_bit_cast(bf16x8, z);
+  }
+  wait_vmcnt<0>();                    // the loop's waits count only LDS loads
+  asm volatile("" ::: "memory");
+  if (klim > 0)
+    dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride, min(BK, klim), lds,
+                wave * C::VBPW, C::VBPW, lane);
+  const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
+  const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
+
+  f32x16 dKt[DB], dVt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dKt[db][i] = dVt[db][i] = 0.f;
+
+  // ---- the query stages of this item, NS-1 stages ahead in an LDS ring
+  StageIter s0;
+  if (it.seg >= 0) {
+    s0.seg = s0.seg_last = it.seg;
+  } else if (it.slot == 0) {
+    s0.seg = s0.seg_last = -1;
+  } else {
+    s0.seg = (it.slot - 1) * sh.per_slot;
+    s0.seg_last = min(pr.N, it.slot * sh.per_slot) - 1;
+  }
+  s0.h0 = s0.h = c * pr.g;
+  s0.h1 = (c + 1) * pr.g;
+  s0.r = 0;
+  s0.ok = false;
+  if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
+  StageIter s1 = s0;
+  if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
+  // NS == 3: stages s0, s1 in flight, s2 issued after the barrier;
+  // NS == 2: s0 in flight, s1 issued after the barrier;
+  // NS == 1: s1 issued once every wave is done with the single buffer.
+  static_assert(NS >= 1 && NS <= 3, "stage ring depth");
+  StageIter s2 = s1;
+  if (NS == 3 && s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+
+  const int64_t qstride = (int64_t)pr.Hq * D;
+  const float c2 = pr.scale * kLog2e;
+  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
+  const bool stat_wave = wave == NWK - 1;    // also loads the stage's lse2 / delta
+
+  // operand bases (bytes from the start of LDS): V rows of this wave's keys;
+  // Q / dO rows l32 of stage 0; Q^T / dO^T transposed reads of stage 0; the
+  // stage's statistics for this lane's rows
+  unsigned vbase = row_base<D>(wk0 + l32, hf);
+  unsigned qbase = V_BYTES + row_base<D>(l32, hf);
+  unsigned tb0, tb1;
+  trans_bases<D>(lane, tb0, tb1);
+  tb0 += V_BYTES;
+  tb1 += V_BYTES;
+  unsigned sbase = V_BYTES + Q_BYTES + DO_BYTES + (unsigned)(4 * hf) * 4u;
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  const unsigned voff = dma_lane_offset<D>(wave, lane, (unsigned)(qstride * 2));
+
+  auto issue = [&](const StageIter& st, int slot) {
+    const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
+    const int n = min(kStageRows, st.svalid - st.r);
+    const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
+    const unsigned dst = lds0 + V_BYTES + (unsigned)slot * STAGE_BYTES + (unsigned)wave * 1024u;
+    // Q block `wave` and dO block `wave` of the stage
+    if (n >= kStageRows) {
+      dma_block(q + off, voff, dst);
+      dma_block(dout + off, voff, dst + Q_BYTES);
+    } else {
+      constexpr int CPR = D / 8, RPB = 64 / CPR;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
+      const int row = wave * RPB + ln / CPR;
+      const int src = min(row, n - 1);
+      const unsigned vo = (unsigned)src * (unsigned)(qstride * 2) + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
+      dma_block(q + off, vo, dst);
+      dma_block(dout + off, vo, dst + Q_BYTES);
+    }
+    if (stat_wave) {
+      // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
+      const int row = sb + st.r + min(lane & 31, n - 1);
+      const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.Tld + row;
+      const unsigned ldsaddr = lds0 + V_BYTES + (unsigned)slot * STAGE_BYTES + Q_BYTES + DO_BYTES;
+      asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
+    }
+  };
+
+  int idx = 0;
+  if (s0.ok) issue(s0, 0);
+  if (NS == 3 && s1.ok) issue(s1, 1);
+  while (s0.ok) {
+    // stage s0 (and the V tile) landed once only s1's loads may be pending
+    if (NS == 3 && s1.ok) {
+      if (stat_wave) wait_vmcnt<C::SBPW + 1>();
+      else wait_vmcnt<C::SBPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_sync();
+    if (NS == 3) {
+      if (s2.ok) issue(s2, (idx + 2) % NS);
+    } else if (NS == 2) {
+      if (s1.ok) issue(s1, (idx + 1) % NS);
+    }
+    {
+      const unsigned so = (unsigned)(idx % NS) * STAGE_BYTES;
+      // per-stage bases (the slot offset is added once; chunk XORs and
+      // immediates reach every operand of the stage)
+      unsigned qb = qbase + so, t0 = tb0 + so, t1 = tb1 + so, sb4 = sbase + so, vb = vbase;
+      asm volatile("" : "+v"(qb), "+v"(t0), "+v"(t1), "+v"(sb4), "+v"(vb));
+      const int s_posoff = s0.seg < 0 ? 0 : pr.P;
+      const int nrows = min(kStageRows, s0.svalid - s0.r);
+      const int sq_lo = s_posoff + s0.r, sq_hi = sq_lo + nrows - 1;
+      // skip / full / masked for this wave's keys against the stage's queries
+      int kind;
+      if (wk_valid <= 0 || nrows <= 0 || sq_hi < wkp_lo || (pr.W > 0 && sq_lo - wkp_hi >= pr.W)) kind = 0;
+      else if (wk_valid == 32 && nrows == kStageRows && sq_lo >= wkp_hi &&
+               (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
+      else kind = 2;
+      if (kind != 0) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        {
+          // S = Q K^T and dP = dO V^T; the operand reads of k-step kk+1 are
+          // issued before the two MFMAs of step kk (scheduling fences)
+          bf16x8 qa = row_operand_x<D>(lds, qb, 0, 0), da = row_operand_x<D>(lds, qb, 0, Q_BYTES);
+          bf16x8 vv = row_operand_x<D>(lds, vb, 0, 0);
+#pragma unroll
+          for (int kk = 0; kk < KT; ++kk) {
+            bf16x8 qn = qa, dn = da, vn = vv;
+            if (kk + 1 < KT) {
+              qn = row_operand_x<D>(lds, qb, kk + 1, 0);
+              dn = row_operand_x<D>(lds, qb, kk + 1, Q_BYTES);
+              vn = row_operand_x<D>(lds, vb, kk + 1, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            s = mfma32(qa, kB[kk], s);
+            dp = mfma32(da, vv, dp);
+            __builtin_amdgcn_sched_barrier(0);
+            qa = qn;
+            da = dn;
+            vv = vn;
+          }
+        }
+        if (kind == 2) {
+          // query qc (+4*hf) of the stage is visible to this lane's key iff
+          // 0 <= qpos - kpos < window and qc < nrows (branch-free); hidden
+          // scores become -inf, so p = exp2(-inf - lse2) = 0 below.
+          int e0 = sq_lo + 4 * hf - kpos;
+          int n0 = (kvalid ? nrows : 0) - 4 * hf;
+          asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qc = 8 * (i >> 2) + (i & 3);           // query row - 4*hf
+            const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
+            s[i] = vis ? s[i] : -INFINITY;
+          }
+        }
+        bf16x8 pB[2], dsB[2];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * g4));
+          const float4 d4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * g4 + kStageRows * 4));
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;                       // register index
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
+            const float ds = p * (dp[i] - dv4[e]);
+            pB[i >> 3][i & 7] = (__bf16)p;
+            dsB[i >> 3][i & 7] = (__bf16)ds;
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 da = trans_operand_x<D>(lds, t0, t1, db, ks, Q_BYTES);
+            const bf16x8 qa = trans_operand_x<D>(lds, t0, t1, db, ks, 0);
+            dVt[db] = mfma32(da, pB[ks], dVt[db]);
+            dKt[db] = mfma32(qa, dsB[ks], dKt[db]);
+          }
+        }
+      }
+    }
+    if (NS == 1) {
+      block_sync();                        // every wave is done with the buffer
+      if (s1.ok) issue(s1, 0);
+    }
+    s0 = s1;
+    if (NS == 3) {
+      s1 = s2;
+      if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+    } else if (s1.ok) {
+      iter_next(pr, s1, kp_lo, kp_hi);
+    }
+    ++idx;
+  }
+
+  // ---- write dK (scaled) and dV for this lane's keys
+  // prompt tiles with response slots write fp32 partials for the reduction
+  const bool partial = it.seg < 0 && sh.slots > 1 && it.k0 >= sh.t0 * BK;
+  {
+    if (my_k < seg_len - it.k0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hf;
+          const f32x16& ak = dKt[db];
+          const f32x16& av = dVt[db];
+          if (partial) {
+            // partials cover prompt rows t0*BK .. P-1 only: [slots, P - t0*BK, Hkv, D]
+            const int prow0 = sh.t0 * BK;
+            const int64_t o =
+                (((int64_t)it.slot * (pr.P - prow0) + it.k0 + my_k - prow0) * pr.Hkv + c) * D + d;
+            *reinterpret_cast<float4*>(part_k + o) =
+                make_float4(ak[4 * g4] * pr.scale, ak[4 * g4 + 1] * pr.scale, ak[4 * g4 + 2] * pr.scale,
+                            ak[4 * g4 + 3] * pr.scale);
+            *reinterpret_cast<float4*>(part_v + o) =
+                make_float4(av[4 * g4], av[4 * g4 + 1], av[4 * g4 + 2], av[4 * g4 + 3]);
+          } else {
+            const int64_t o = krow * kstride + (int64_t)c * D + d;
+            union { __bf16 h[4]; uint2 u; } pk, pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pk.h[e] = (__bf16)(ak[4 * g4 + e] * pr.scale);
+              pv.h[e] = (__bf16)av[4 * g4 + e];
+            }
+            *reinterpret_cast<uint2*>(dk + o) = pk.u;
+            *reinterpret_cast<uint2*>(dv + o) = pv.u;
+          }
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------- preprocess
 //
 // Per query row and head: Delta = sum_d dO * O (fp32) and lse2 = LSE * log2(e)
@@ -747,8 +1074,10 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
                char* ws, hipStream_t stream) {
   using CK = KvCfg<D, NWK, KVNS, KDS, VREG, KW>;
   static_assert(CK::LDS_BYTES <= 160 * 1024, "LDS budget");
-  static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
-  if (a2 != hipSuccess) return a2;
+  if constexpr (!(D == 128 && KDS == 1 && !VREG && KW == 1)) {
+    static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
+    if (a2 != hipSuccess) return a2;
+  }
   float* delta = reinterpret_cast<float*>(ws + p.off_delta);
   float* lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
   float* pk = reinterpret_cast<float*>(ws + p.off_pk);
@@ -774,9 +1103,14 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), CK::LDS_BYTES,
-               stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
-               static_cast<uint16_t*>(dv), pk, pv);
+    if constexpr (D == 128 && KDS == 1 && !VREG && KW == 1)
+      e = launch("bwd_dkdv", bwd_dkdv_lean_kernel<D, NWK, KVNS>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), 0,
+                 stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
+                 static_cast<uint16_t*>(dv), pk, pv);
+    else
+      e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64),
+                 CK::LDS_BYTES, stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
+                 static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
   }
   if (p.reduce) {
