@@ -391,8 +391,11 @@ struct LeanCfg {
   static constexpr int V_REGION = NS * TILE_BYTES;  // V slots start here
   static constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
   static constexpr int KBLK = TILE_BYTES / 1024;    // 1 KiB blocks per tile
-  static constexpr int BPW = KBLK / NW;             // blocks per wave per tile (K and V each)
-  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
+  // waves that load tiles (the first NWL): the largest power of two <= NW
+  // that divides the tile's blocks
+  static constexpr int NWL = NW >= KBLK ? KBLK : NW >= 8 ? 8 : NW >= 4 ? 4 : NW >= 2 ? 2 : 1;
+  static constexpr int BPW = KBLK / NWL;            // blocks per loading wave per tile (K and V each)
+  static_assert(KBLK % NWL == 0, "tile blocks must split evenly over the loading waves");
   static_assert(V_REGION + (NS - 1) * TILE_BYTES <= 65536 + V_REGION, "immediate offsets reach every slot");
 };
 
@@ -476,6 +479,7 @@ __global__ void __launch_bounds__(NW * 64)
     for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::BPW + j, lane, row_bytes);
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     auto issue = [&](int t) {
+      if (C::NWL < NW && wave >= C::NWL) return;    // not a loading wave
       const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
       const unsigned kdst = lds0 + (unsigned)((t % NS) * C::TILE_BYTES + wave * C::BPW * 1024);
@@ -650,10 +654,11 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
   // D = 512 over groups of four waves, so every head dim runs eight waves,
   // two per SIMD (at D = 512 four-way instead of two-way with one wave per
   // SIMD: 12% less forward time on the Gemma-style global layer).
-  p.NW = 8;
+  p.NW = pr.D == 128 ? 12 : 8;
   p.BN = pr.D <= 128 ? 64 : 32;
   p.DS = pr.D <= 128 ? 1 : pr.D == 256 ? 2 : 4;
-  p.HG = heads_per_block(pr.g, p.NW / p.DS);
+  p.HG = 1;   // query heads per block: a power of two dividing g and the waves' row slots
+  while (p.HG * 2 <= p.NW / p.DS && pr.g % (p.HG * 2) == 0 && (p.NW / p.DS) % (p.HG * 2) == 0) p.HG *= 2;
   p.BM = 32 * (p.NW / p.DS) / p.HG;
   int64_t nb = 0;
   for (int i = 0; i < G.n; ++i) {
@@ -703,7 +708,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   if (p.nwg == 0) return hipSuccess;
   switch (pr.D) {
     case 64: return run_lean<64, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
-    case 128: return run_lean<128, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
+    case 128: return run_lean<128, 64, 12, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 256: return run<256, 32, 8, 3, 2>(pr, G, p, q, k, v, o, lse, stream);
     case 512: return run<512, 32, 8, 2, 4>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
