@@ -64,20 +64,48 @@ def timed(fn, steps, torch):
     return s.elapsed_time(e) / steps
 
 
+def _cpu_description():
+    """CPU model, affinity core count and BLAS library of this host."""
+    import os
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)" for i in info)
+    threads = max((i.get("num_threads", 1) for i in info), default=1)
+    return model, len(os.sched_getaffinity(0)), blas or "unknown", int(threads)
+
+
 def cpu_baseline(w, groups, x, seconds):
     """The fp64 oracle on a bounded sample: the replicated sequences of the
     groups in order (group 0's n = 0, 1, ..., then group 1's ...), KV head 0
     (all its query heads), forward + backward, until `seconds` have passed.
-    Rate in useful TFLOP/s of the pairs computed."""
+    The sample's time is scaled to the whole job (every sequence, every KV
+    head; the work of a sequence and head is proportional to its visible
+    replicated pairs) and `value` is the job's useful FLOPs of the packed
+    layout (the GPU metric's count) over that extrapolated time."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import replicated
     from shared_prompt_exact_amd import workcount
 
     g = w.n_q_heads // w.n_kv_heads
     total = sum(N for N, _, _ in groups)
-    done, t0, flops, row0, vl0 = 0, time.perf_counter(), 0, 0, 0
+    done, t0, pairs_done, row0, vl0 = 0, time.perf_counter(), 0, 0, 0
+    pairs_all = packed_all = 0
+    for N, P, R in groups:
+        L = [R] * N if x.valid_len is None else [int(a) for a in x.valid_len[vl0:vl0 + N]]
+        pairs_all += workcount.replicated_pairs(N, P, R, w.window, L)
+        packed_all += workcount.visible_pairs(N, P, R, w.window, L)
+        vl0 += N
+    vl0 = 0
     for N, P, R in groups:
         L = [R] * N if x.valid_len is None else [int(a) for a in x.valid_len[vl0:vl0 + N]]
         for n in range(N):
@@ -85,7 +113,7 @@ def cpu_baseline(w, groups, x, seconds):
             replicated.causal_sequence(x.q[idx].astype(np.float64), x.k[idx].astype(np.float64),
                                        x.v[idx].astype(np.float64), x.do[idx].astype(np.float64),
                                        P + L[n], w.window, None, 1024, kv_heads=[0])
-            flops += 14 * workcount.replicated_pairs(1, P, L[n], w.window) * g * w.head_dim
+            pairs_done += workcount.replicated_pairs(1, P, L[n], w.window)
             done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
@@ -94,11 +122,18 @@ def cpu_baseline(w, groups, x, seconds):
         row0 += P + N * R
         vl0 += N
     dt = time.perf_counter() - t0
-    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    t_job = dt * (pairs_all / max(pairs_done, 1)) * w.n_kv_heads
+    useful = 14 * packed_all * w.n_q_heads * w.head_dim
+    model, affinity, blas, threads = _cpu_description()
+    return {"value": useful / t_job / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"fp64 oracle (replicated causal attention + analytic backward), KV head 0 "
                        f"of {w.n_kv_heads} with its {g} query heads, {done} of {total} sequences "
-                       f"(prompt + response), {dt:.1f} s; rate counts useful pairs of the sample")}
+                       f"(prompt + response) in {dt:.1f} s; extrapolated to the whole job "
+                       f"(all sequences and KV heads, by visible replicated pairs): {t_job:.0f} s; "
+                       f"value = the job's useful packed-layout FLOPs / that time"),
+            "extrapolated": True, "sample_s": round(dt, 2), "job_s_extrapolated": round(t_job, 1),
+            "sample_rate_replicated_tflops": 14 * pairs_done * g * w.head_dim / dt / 1e12,
+            "cpu_model": model, "affinity_cores": affinity, "blas": blas}
 
 
 # Decoder-layer shapes of the attention workloads (hidden size, MLP width,

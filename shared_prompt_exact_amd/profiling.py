@@ -5,6 +5,11 @@ Two summaries, both written as short markdown under ``profiles/``:
 * ``kernels``: a ``rocprofv3 --kernel-trace --stats --output-format csv`` run
   of ``bench.py`` -> per-kernel call counts and durations, next to the
   library's own event timings printed by the same run (its JSON line).
+* ``counters``: three ``rocprofv3 --pmc`` runs of bench.py (the counter sets
+  PASSES below, each within one run's hardware limits) -> per kernel the
+  matrix-core and vector-ALU busy fractions, how much of the matrix-core
+  busy time also issued vector instructions (co-execution), LDS activity
+  and bank conflicts, occupancy, and instruction counts per MFMA.
 * ``traffic``: two ``rocprofv3 --pmc`` runs of the same command, one with
   FETCH_SIZE and one with WRITE_SIZE (KiB per dispatch) -> HBM bytes per
   launch of one kernel.  Each counter is scaled by the factor that makes it
@@ -17,6 +22,7 @@ Two summaries, both written as short markdown under ``profiles/``:
 Usage (repo root):
   python3 -m shared_prompt_exact_amd.profiling kernels STATS_DIR BENCH_LOG OUT.md TITLE CMD
   python3 -m shared_prompt_exact_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL WORKLOAD OUT.md CMD_FETCH CMD_WRITE
+  python3 -m shared_prompt_exact_amd.profiling counters OUT.md TITLE DIR_A DIR_B DIR_C CMD_A CMD_B CMD_C
 """
 from __future__ import annotations
 
@@ -31,12 +37,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "shared_prompt_exact_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
-# library kernel name -> (substring of the device symbol, source files it is built from)
+# library kernel name -> (substrings of the device symbols, source files they are built from)
 _HEADERS = ["common.h", "mfma_common.h", "lds_tiles.h"]
 KERNELS = {
-    "fwd": ("fwd_mfma_kernel", ["attn_fwd_mfma.hip"] + _HEADERS),
-    "bwd_dq": ("bwd_dq_kernel", ["attn_bwd_dq.hip"] + _HEADERS),
-    "bwd_dkdv": ("bwd_dkdv_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
+    "fwd": (("fwd_mfma_kernel", "fwd_lean_kernel"), ["attn_fwd_mfma.hip"] + _HEADERS),
+    "bwd_dq": (("bwd_dq_kernel", "bwd_dq_lean_kernel"), ["attn_bwd_dq.hip"] + _HEADERS),
+    "bwd_dkdv": (("bwd_dkdv_kernel", "bwd_dkdv_lean_kernel"), ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_reduce": ("reduce_slots_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_delta": ("delta_lse2_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "repack": ("repack_kernel", ["repack.hip", "common.h"]),
@@ -60,9 +66,10 @@ def source_hash(kernel: str) -> str:
 
 
 def short_name(symbol: str) -> str:
-    for k, (sub, _) in KERNELS.items():
-        if sub in symbol:
-            return k
+    for k, (subs, _) in KERNELS.items():
+        for sub in (subs if isinstance(subs, tuple) else (subs,)):
+            if sub in symbol:
+                return k
     return "other"
 
 
@@ -149,6 +156,75 @@ def traffic_summary(fetch_dir, write_dir, kernel, workload, out_path, cmd_fetch,
     return "\n".join(out)
 
 
+# Counter sets of the ``counters`` summary, one rocprofv3 --pmc run each.
+# A: rocprofv3's derived metrics (their formulas as `rocprofv3 -L` lists
+#    them on MI355X): MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE
+#    x SIMDs); VALUBusy = SQ_ACTIVE_INST_VALU / (CUs x GRBM_GUI_ACTIVE);
+#    LdsUtil = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE x CUs); LDSBankConflict =
+#    SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs; OccupancyPercent = 400 x
+#    SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32 (of 32 waves per CU).
+# B, C: raw SQ counters, used as ratios (per MFMA instruction, or co-issue
+#    cycles over matrix-core busy cycles).
+PASSES = {
+    "A": ["MfmaUtil", "VALUBusy", "LdsUtil", "LDSBankConflict", "OccupancyPercent"],
+    "B": ["SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+          "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"],
+    "C": ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC",
+          "SQ_INSTS_SALU", "SQ_ACTIVE_INST_VALU2", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+
+
+def _counter_means(d: str) -> dict:
+    """kernel short name -> symbol, counter -> mean over the kernel's dispatches."""
+    acc: dict = {}
+    for r in _csv(d, "counter_collection.csv"):
+        k = short_name(r["Kernel_Name"])
+        sym = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace(
+            "dualkv::", "")
+        e = acc.setdefault(k, {"symbol": sym, "vals": {}})
+        e["vals"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {"symbol": e["symbol"], **{c: sum(v) / len(v) for c, v in e["vals"].items()}}
+            for k, e in acc.items()}
+
+
+def counters_summary(out_path, title, dir_a, dir_b, dir_c, cmd_a, cmd_b, cmd_c):
+    merged: dict = {}
+    for d in (dir_a, dir_b, dir_c):
+        for k, vals in _counter_means(d).items():
+            merged.setdefault(k, {}).update(vals)
+    rows = []
+    for k in ("fwd", "bwd_dq", "bwd_dkdv", "bwd_delta", "bwd_reduce", "gemm"):
+        if k not in merged:
+            continue
+        m = merged[k]
+        mf = max(m.get("SQ_INSTS_MFMA", 0.0), 1.0)
+        busy = max(m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), 1.0)
+        rows.append((k, m["symbol"], m.get("MfmaUtil", float("nan")), m.get("VALUBusy", float("nan")),
+                     m.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / busy, m.get("LdsUtil", float("nan")),
+                     m.get("LDSBankConflict", float("nan")), m.get("OccupancyPercent", float("nan")) * 8 / 100,
+                     (m.get("SQ_INSTS_VALU", 0.0) - m.get("SQ_INSTS_MFMA", 0.0)) / mf,
+                     m.get("SQ_INSTS_VALU_TRANS_F32", 0.0) / mf, m.get("SQ_INSTS_LDS", 0.0) / mf,
+                     m.get("SQ_INSTS_SALU", 0.0) / mf))
+    out = [f"# {title}", "", "Commands (repo root, MI355X), one counter set per run:", "",
+           "    " + cmd_a, "    " + cmd_b, "    " + cmd_c, "",
+           "Per kernel, means over its dispatches in the profiled steps.  MFMA and VALU busy are % of the "
+           "kernel's cycles on all SIMDs; co-exec is the share of matrix-core busy cycles in which a "
+           "vector instruction also issued; waves/SIMD is the mean occupancy; the last columns are "
+           "instructions per MFMA instruction (VALU excluding MFMA, of them transcendental, LDS, scalar).",
+           "",
+           "| kernel | symbol | MFMA busy % | VALU busy % | co-exec | LDS busy % | LDS bank conflict % | "
+           "waves/SIMD | VALU/MFMA | trans/MFMA | LDS/MFMA | SALU/MFMA |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r[0]} | `{r[1]}` | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.3f} | {r[5]:.1f} | {r[6]:.2f} | "
+                   f"{r[7]:.2f} | {r[8]:.2f} | {r[9]:.2f} | {r[10]:.2f} | {r[11]:.2f} |")
+    out += ["", "```json", json.dumps({k: {c: v for c, v in merged[k].items()} for k in merged if k != "other"},
+                                      indent=1, sort_keys=True), "```", ""]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(out))
+    return "\n".join(out)
+
+
 def load_traffic(kernel: str, workload: str):
     """The calibrated HBM bytes per launch recorded for `kernel` on `workload`,
     or None when there is no record or the kernel's sources have changed."""
@@ -172,6 +248,8 @@ def main(argv):
         print(kernels_summary(*argv[1:6]))
     elif len(argv) >= 8 and argv[0] == "traffic":
         print(traffic_summary(*argv[1:8]))
+    elif len(argv) >= 9 and argv[0] == "counters":
+        print(counters_summary(*argv[1:9]))
     else:
         print(__doc__)
         return 2

@@ -50,3 +50,27 @@ def test_committed_records_parse():
             text = open(os.path.join(profiling.PROFILES, f)).read()
             rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
             assert rec["bytes_per_launch"] > 0 and rec["kernel"] in profiling.KERNELS
+
+
+def test_counters_summary(tmp_path):
+    fwd = "void dualkv::(anonymous namespace)::fwd_lean_kernel<128, 64, 12, 3>(...)"
+    dkdv = "void dualkv::(anonymous namespace)::bwd_dkdv_lean_kernel<128, 8, 3>(...)"
+    def put(d, rows):
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+            wr = csv.DictWriter(fh, fieldnames=COLS)
+            wr.writeheader()
+            for i, (name, c, v) in enumerate(rows, 1):
+                wr.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    put(tmp_path / "a", [(fwd, "MfmaUtil", 50.0), (fwd, "OccupancyPercent", 37.5), (dkdv, "MfmaUtil", 40.0)])
+    put(tmp_path / "b", [(fwd, "SQ_INSTS_MFMA", 100.0), (fwd, "SQ_INSTS_VALU", 600.0),
+                         (fwd, "SQ_VALU_MFMA_BUSY_CYCLES", 3200.0), (fwd, "SQ_VALU_MFMA_COEXEC_CYCLES", 800.0)])
+    put(tmp_path / "c", [(fwd, "SQ_INSTS_SALU", 200.0)])
+    out = tmp_path / "c.md"
+    text = profiling.counters_summary(str(out), "t", str(tmp_path / "a"), str(tmp_path / "b"),
+                                      str(tmp_path / "c"), "x", "y", "z")
+    row = [ln for ln in text.splitlines() if ln.startswith("| fwd |")][0].split("|")
+    # MFMA busy 50, co-exec 800/3200, 3 waves per SIMD, (600-100)/100 VALU per MFMA, 2 SALU per MFMA
+    assert float(row[3]) == 50.0 and float(row[5]) == 0.25 and float(row[8]) == 3.0
+    assert float(row[9]) == 5.0 and float(row[12]) == 2.0
+    assert any(ln.startswith("| bwd_dkdv |") for ln in text.splitlines())
