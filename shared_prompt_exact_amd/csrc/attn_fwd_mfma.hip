@@ -656,7 +656,7 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
   // SIMD: 12% less forward time on the Gemma-style global layer).
   p.NW = pr.D == 128 ? 12 : 8;
   p.BN = pr.D <= 128 ? 64 : 32;
-  p.DS = pr.D <= 128 ? 1 : pr.D == 256 ? 2 : 4;
+  p.DS = pr.D <= 256 ? 1 : 4;
   p.HG = 1;   // query heads per block: a power of two dividing g and the waves' row slots
   while (p.HG * 2 <= p.NW / p.DS && pr.g % (p.HG * 2) == 0 && (p.NW / p.DS) % (p.HG * 2) == 0) p.HG *= 2;
   p.BM = 32 * (p.NW / p.DS) / p.HG;
@@ -709,7 +709,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   switch (pr.D) {
     case 64: return run_lean<64, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 128: return run_lean<128, 64, 12, 3>(pr, G, p, q, k, v, o, lse, stream);
-    case 256: return run<256, 32, 8, 3, 2>(pr, G, p, q, k, v, o, lse, stream);
+    case 256: return run_lean<256, 32, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 512: return run<512, 32, 8, 2, 4>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
