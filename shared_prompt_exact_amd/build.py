@@ -16,23 +16,27 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdualkv.so")
-SOURCES = ["repack.hip", "attn_scalar.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq.hip", "api.hip", "profile.hip",
-           "gemm.hip", "layer_ops.hip", "layer.hip"]
+SOURCES = ["repack.hip", "attn_scalar.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq.hip",
+           "attn_bwd_dq_wide.hip", "api.hip", "profile.hip", "gemm.hip", "layer_ops.hip", "layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-I" + os.path.join(ROOT, "include"),
     # keep the compiler from forming packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in ordinary VGPRs (accumulation registers then serve as
-    # overflow): the head-dim-split kernels stop spilling to scratch
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# MFMA results in ordinary VGPRs (accumulation registers then serve as
+# overflow): the kernels of two waves per SIMD stop spilling to scratch.
+# Not for the one-wave-per-SIMD kernels whose accumulators live in the
+# accumulation registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACCUMULATORS = {"attn_bwd_dq_wide.hip"}
 
 
 def _compile(src: str) -> tuple[str, int, str]:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [] if src in AGPR_ACCUMULATORS else VGPR_FORM
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(line for line in (p.stdout + p.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in line)

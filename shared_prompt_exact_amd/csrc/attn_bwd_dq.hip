@@ -387,10 +387,6 @@ template hipError_t launch_bwd_dq<128, 32, 8, 3, 1>(const Problem&, const Groups
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);
-template hipError_t launch_bwd_dq<256, 32, 4, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
-                                                    const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
-                                                    uint16_t*, hipStream_t);
 template hipError_t launch_bwd_dq<512, 32, 8, 2, 4>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,

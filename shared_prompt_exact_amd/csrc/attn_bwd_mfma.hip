@@ -1097,9 +1097,13 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_dq > 0) {
-    e = launch_bwd_dq<D, kDqBN, NW, DQNS, DS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16,
-                                               static_cast<const uint16_t*>(o), lse, delta, lse2,
-                                               static_cast<uint16_t*>(dq), stream);
+    if constexpr (D == 256 && DS == 1 && NW == 4)
+      e = launch_bwd_dq_wide(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16, static_cast<const uint16_t*>(o),
+                             lse, delta, lse2, static_cast<uint16_t*>(dq), stream);
+    else
+      e = launch_bwd_dq<D, kDqBN, NW, DQNS, DS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16,
+                                                 static_cast<const uint16_t*>(o), lse, delta, lse2,
+                                                 static_cast<uint16_t*>(dq), stream);
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {

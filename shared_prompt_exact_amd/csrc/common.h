@@ -148,6 +148,13 @@ hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& 
                          const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
                          hipStream_t stream);
 
+// dQ kernel at head dim 256, one wave per SIMD (attn_bwd_dq_wide.hip); forms
+// Delta and LSE*log2(e) like the DS == 1 configurations above.
+hipError_t launch_bwd_dq_wide(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
+                              const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                              const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
+                              hipStream_t stream);
+
 // Scalar backward: delta[h][t] = sum_d dO[t,h,d] * O[t,h,d] in fp32 (0 on
 // rows with no visible key) for all pr.Tld rows.
 hipError_t launch_bwd_delta(const Problem& pr, int dtype, const void* o, const void* dout,

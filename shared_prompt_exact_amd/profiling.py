@@ -41,7 +41,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 _HEADERS = ["common.h", "mfma_common.h", "lds_tiles.h"]
 KERNELS = {
     "fwd": (("fwd_mfma_kernel", "fwd_lean_kernel"), ["attn_fwd_mfma.hip"] + _HEADERS),
-    "bwd_dq": (("bwd_dq_kernel", "bwd_dq_lean_kernel"), ["attn_bwd_dq.hip"] + _HEADERS),
+    "bwd_dq": (("bwd_dq_kernel", "bwd_dq_lean_kernel", "bwd_dq_wide_kernel"), ["attn_bwd_dq.hip", "attn_bwd_dq_wide.hip"] + _HEADERS),
     "bwd_dkdv": (("bwd_dkdv_kernel", "bwd_dkdv_lean_kernel"), ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_reduce": ("reduce_slots_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_delta": ("delta_lse2_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
