@@ -59,8 +59,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
   const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;                          // grid padding (whole workgroup)
   const int hgi = L / NB;
-  const int gi = group_of(GB.off, G.n, L % NB);
-  const int blk = L % NB - GB.off[gi];
+  int blk;
+  const int gi = order_lookup(GB.ord, L % NB, blk);
   const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
   const Problem pr = group_problem(pa, G, gi);
   {

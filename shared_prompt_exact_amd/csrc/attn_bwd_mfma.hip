@@ -89,7 +89,10 @@ struct KvGroups {
   int off[kMaxGroups + 1];
   KvShape sh[kMaxGroups];
   int64_t part[kMaxGroups];
+  LaunchOrder ord;    // places the groups' items in the launch
 };
+static_assert(sizeof(Problem) + sizeof(Groups) + sizeof(KvGroups) + 16 * sizeof(void*) <= 4096,
+              "dK/dV kernel arguments");
 
 // Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
 // positions) of the item; lo is rounded down to a stage boundary.
@@ -166,8 +169,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   KvItem it;
   it.c = Lid / per_head;
   int x = Lid % per_head;
-  const int gi = group_of(KG.off, G.n, x);
-  x -= KG.off[gi];
+  const int gi = order_lookup(KG.ord, x, x);
   const Problem pr = group_problem(pa, G, gi);
   const KvShape sh = KG.sh[gi];
   {
@@ -575,8 +577,7 @@ __global__ void __launch_bounds__(NWK * 64)
   KvItem it;
   it.c = Lid / per_head;
   int x = Lid % per_head;
-  const int gi = group_of(KG.off, G.n, x);
-  x -= KG.off[gi];
+  const int gi = order_lookup(KG.ord, x, x);
   const Problem pr = group_problem(pa, G, gi);
   const KvShape sh = KG.sh[gi];
   {
@@ -1015,6 +1016,28 @@ KvShape kv_shape(int N, int P, int R, int W, int BK) {
   return sh;
 }
 
+// Query rows that item j of a group streams (the kernel's item order:
+// response slots of the prompt tiles, the prompt slot of every prompt
+// tile, then the response key tiles).
+double kv_item_cost(const KvShape& sh, int N, int P, int R, int W, int BK, int j) {
+  const int64_t nPtR = sh.nPt - sh.t0;
+  int64_t rows;
+  if (j < nPtR * (sh.slots - 1)) {
+    const int slot = 1 + (int)(j / nPtR);
+    const int64_t k_end = (int64_t)(sh.t0 + j % nPtR + 1) * BK;
+    const int64_t resp = std::min<int64_t>(sh.per_slot, (int64_t)N - (int64_t)(slot - 1) * sh.per_slot);
+    const int64_t per = W > 0 ? std::min<int64_t>(R, std::max<int64_t>(0, W - (P - k_end))) : R;
+    rows = resp * per;
+  } else if (j < nPtR * (sh.slots - 1) + sh.nPt) {
+    const int64_t k0 = (j - nPtR * (sh.slots - 1)) * BK;
+    rows = W > 0 ? std::min<int64_t>(P - k0, (int64_t)W + BK) : P - k0;
+  } else {
+    const int64_t k0 = ((j - nPtR * (sh.slots - 1) - sh.nPt) / N) * BK;
+    rows = W > 0 ? std::min<int64_t>(R - k0, (int64_t)W + BK) : R - k0;
+  }
+  return (double)rows;
+}
+
 BwdPlan plan(const Problem& pr, const Groups& G) {
   BwdPlan p;
   p.NW = dq_waves(pr.D);
@@ -1057,6 +1080,18 @@ BwdPlan plan(const Problem& pr, const Groups& G) {
   }
   p.gb.off[G.n] = (int)std::min(nb, kBig);
   p.kg.off[G.n] = (int)std::min(items, kBig);
+  int64_t cnt[kMaxGroups];
+  for (int i = 0; i < G.n; ++i) cnt[i] = (int64_t)p.gb.nbP[i] + (int64_t)G.N[i] * p.gb.nbR[i];
+  p.gb.ord = make_order(cnt, G.n, [&](int i, int j) {
+    return row_block_cost(G.N[i], G.P[i], G.R[i], pr.W, p.BM, p.gb.nbP[i], p.gb.nbR[i], j);
+  });
+  for (int i = 0; i < G.n; ++i) {
+    const KvShape& sh = p.kg.sh[i];
+    cnt[i] = (int64_t)(sh.nPt - sh.t0) * (sh.slots - 1) + sh.nPt + (int64_t)G.N[i] * sh.nRt;
+  }
+  p.kg.ord = make_order(cnt, G.n, [&](int i, int j) {
+    return kv_item_cost(p.kg.sh[i], G.N[i], G.P[i], G.R[i], pr.W, BK, j);
+  });
   p.nwg_dq = nb >= kBig ? ((int64_t)1 << 40) : balanced_grid(pr.Hq / p.HG, nb);
   p.nwg_kv = items >= kBig ? ((int64_t)1 << 40) : balanced_grid(pr.Hkv, items);
   p.red_blocks = std::min<int64_t>(std::max<int64_t>((red + 255) / 256, 1), std::max(1, 4096 / G.n));

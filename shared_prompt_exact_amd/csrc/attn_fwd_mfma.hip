@@ -86,8 +86,8 @@ __global__ void __launch_bounds__(NW * 64)
   if (L < 0) return;                            // grid padding (whole workgroup)
   const int hgi = L / NB;
   // the prompt group of this block; rows and statistics below are the group's
-  const int gi = group_of(GB.off, G.n, L % NB);
-  const int blk = L % NB - GB.off[gi];
+  int blk;
+  const int gi = order_lookup(GB.ord, L % NB, blk);
   const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
   const Problem pr = group_problem(pa, G, gi);
   {
@@ -415,8 +415,8 @@ __global__ void __launch_bounds__(NW * 64)
   const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;
   const int hgi = L / NB;
-  const int gi = group_of(GB.off, G.n, L % NB);
-  const int blk = L % NB - GB.off[gi];
+  int blk;
+  const int gi = order_lookup(GB.ord, L % NB, blk);
   const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
   const Problem pr = group_problem(pa, G, gi);
   {
@@ -641,6 +641,9 @@ __global__ void __launch_bounds__(NW * 64)
   }
 }
 
+static_assert(sizeof(Problem) + sizeof(Groups) + sizeof(GroupBlocks) + 8 * sizeof(void*) <= 4096,
+              "forward kernel arguments");
+
 struct FwdPlan {
   int NW, BN, DS, HG, BM;
   GroupBlocks gb;
@@ -668,6 +671,11 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
     nb += p.gb.nbP[i] + (int64_t)G.N[i] * p.gb.nbR[i];
   }
   p.gb.off[G.n] = (int)std::min<int64_t>(nb, INT32_MAX);
+  int64_t cnt[kMaxGroups];
+  for (int i = 0; i < G.n; ++i) cnt[i] = (int64_t)p.gb.nbP[i] + (int64_t)G.N[i] * p.gb.nbR[i];
+  p.gb.ord = make_order(cnt, G.n, [&](int i, int j) {
+    return row_block_cost(G.N[i], G.P[i], G.R[i], pr.W, p.BM, p.gb.nbP[i], p.gb.nbR[i], j);
+  });
   p.nwg = nb >= INT32_MAX ? ((int64_t)1 << 40) : balanced_grid(pr.Hq / p.HG, nb);
   return p;
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "dualkv.h"
 
 namespace dualkv {
@@ -46,18 +48,92 @@ __host__ __device__ inline Problem group_problem(const Problem& base, const Grou
   return p;
 }
 
-// Logical blocks of a launch per group: group i owns [off[i], off[i+1]).
+// Order of a launch's work items across its groups.  Each group lists its
+// items longest first; the launch cuts every group's list into at most
+// kMaxChunks / n chunks of consecutive items and runs the chunks of all
+// groups by decreasing cost of their first (longest) item, so the short
+// items of every group meet at the end of the launch instead of each
+// group's tail sitting between the next group's long items.  Chunk i covers
+// launch positions [start[i], start[i+1]) and holds items loc[i] .. of
+// group grp[i].
+constexpr int kMaxChunks = 48;
+struct LaunchOrder {
+  int n;
+  int start[kMaxChunks + 1];
+  int loc[kMaxChunks];
+  uint8_t grp[kMaxChunks];
+};
+
+// Group and item of launch position x (a binary search over at most
+// kMaxChunks entries, scalar registers only).
+__device__ __forceinline__ int order_lookup(const LaunchOrder& o, int x, int& item) {
+  int lo = 0, hi = o.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (o.start[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  item = o.loc[lo] + (x - o.start[lo]);
+  return o.grp[lo];
+}
+
+// Builds the order from the groups' item counts and a cost of item j of
+// group i (cost(i, j) non-increasing in j).  One group keeps its own order.
+// Equal costs keep group order (stable sort).
+template <class Cost>
+LaunchOrder make_order(const int64_t* count, int ngroups, Cost cost) {
+  LaunchOrder o{};
+  struct Chunk { double cost; int g, loc, len; };
+  Chunk ch[kMaxChunks];
+  int nc = 0;
+  const int per = ngroups > 0 ? kMaxChunks / ngroups : 1;
+  for (int i = 0; i < ngroups; ++i) {
+    const int64_t m = count[i];
+    const int64_t k = m < per ? m : per;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t a = m * j / k, b = m * (j + 1) / k;
+      if (b > a) ch[nc++] = Chunk{cost(i, (int)a), i, (int)a, (int)(b - a)};
+    }
+  }
+  if (nc == 0) ch[nc++] = Chunk{0.0, 0, 0, 0};
+  for (int i = 1; i < nc; ++i)   // stable insertion sort, decreasing cost
+    for (int j = i; j > 0 && ch[j - 1].cost < ch[j].cost; --j) {
+      const Chunk t = ch[j];
+      ch[j] = ch[j - 1];
+      ch[j - 1] = t;
+    }
+  o.n = nc;
+  int pos = 0;
+  for (int i = 0; i < nc; ++i) {
+    o.start[i] = pos;
+    o.loc[i] = ch[i].loc;
+    o.grp[i] = (uint8_t)ch[i].g;
+    pos += ch[i].len;
+  }
+  o.start[nc] = pos;
+  return o;
+}
+
+// Logical blocks of a launch per group: group i owns off[i+1] - off[i]
+// blocks; `ord` places them in the launch.
 struct GroupBlocks {
   int off[kMaxGroups + 1];
   int nbP[kMaxGroups], nbR[kMaxGroups];   // prompt / response row blocks (query-parallel kernels)
+  LaunchOrder ord;
 };
 
-// Group of logical block x (a linear scan: at most kMaxGroups entries,
-// scalar registers only).
-__device__ __forceinline__ int group_of(const int* off, int n, int x) {
-  int gi = 0;
-  while (gi + 1 < n && x >= off[gi + 1]) ++gi;
-  return gi;
+// Cost (visible keys of its last query) of row block j of a group in the
+// query-parallel kernels' order (decode_block): response blocks from the
+// last down, then prompt blocks from the last down.
+inline double row_block_cost(int N, int P, int R, int W, int BM, int nbP, int nbR, int j) {
+  int64_t q_end;
+  if (j < (int64_t)N * nbR) {
+    const int rb = nbR - 1 - j / N;
+    q_end = (int64_t)P + std::min<int64_t>((int64_t)(rb + 1) * BM, R);
+  } else {
+    const int pb = nbP - 1 - (j - N * nbR);
+    q_end = std::min<int64_t>((int64_t)(pb + 1) * BM, P);
+  }
+  return (double)(W > 0 ? std::min<int64_t>(q_end, (int64_t)W + BM - 1) : q_end);
 }
 
 __device__ __forceinline__ int resp_valid(const Problem& pr, int n) {

@@ -45,6 +45,10 @@ CASES = [
     # head dims 256 (window) and 512
     GW("grp_d256", "bf16", ((2, 90, 70), (2, 150, 40)), 4, 2, 256, 40, seed=54, value_scale=1.0),
     GW("grp_d512", "bf16", ((2, 70, 45), (1, 40, 30)), 4, 1, 512, seed=55, value_scale=1.0),
+    # groups whose cost ranges interleave (a long-prompt group, a long-response
+    # group, many short responses), so the launch order mixes their chunks
+    GW("grp_order", "bf16", ((12, 520, 64), (2, 64, 900), (5, 300, 33)), 4, 1, 128, seed=59,
+       value_scale=1.0, len_ranges=((1, 64), (500, 900), (1, 33))),
     # the maximum number of groups, small and ragged
     GW("grp_max", "bf16", _many_groups(dk.MAX_GROUPS, 56), 4, 2, 128, seed=56, value_scale=1.0),
     # the scalar fp32 path
@@ -74,8 +78,38 @@ def test_groups_match_oracle(w):
     print({k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in out.items()}, flush=True)
 
 
-@pytest.mark.parametrize("w", [CASES[0], CASES[1], CASES[4], CASES[5], CASES[6]],
-                         ids=["grp_mix", "grp_window", "grp_d512", "grp_max", "grp_f32"])
+def _case(name):
+    return next(c for c in CASES if c.name == name)
+
+
+@pytest.mark.parametrize("name", ["grp_mix", "grp_order", "grp_d512", "grp_max", "grp_window"])
+def test_groups_write_every_output(name):
+    """Every output element is written exactly by the grouped launches
+    (outputs and workspace start as NaN): the launch order that interleaves
+    the groups' work items reaches every item."""
+    w = _case(name)
+    print(f"case {w.name} groups={w.groups}", flush=True)
+    x = workloads.generate_groups(w)
+    d = inputs_on_device(w, x)
+    kw = dict(window=w.window, valid_len=d["valid"])
+    nan = float("nan")
+    o = torch.full_like(d["q"], nan)
+    lse = torch.full((d["q"].shape[1], d["q"].shape[0]), nan, dtype=torch.float32, device=d["q"].device)
+    dk.dualkv_fwd_groups(d["q"], d["k"], d["v"], w.groups, out=o, lse=lse, **kw)
+    need = dk.dualkv_bwd_groups_workspace_bytes(d["q"], d["k"], w.groups, **kw)
+    ws = torch.full((max(need, 256),), 255, dtype=torch.uint8, device=d["q"].device)
+    grads = [torch.full_like(d[n], nan) for n in ("q", "k", "v")]
+    dk.dualkv_bwd_groups(d["q"], d["k"], d["v"], o, lse, d["do"], w.groups, workspace=ws, dq=grads[0],
+                         dk=grads[1], dv=grads[2], **kw)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    for name_, t in zip(("o", "dq", "dk", "dv"), [o] + grads):
+        assert torch.isfinite(t).all(), name_
+
+
+@pytest.mark.parametrize("w", [_case(n) for n in ("grp_mix", "grp_window", "grp_order", "grp_d512", "grp_max",
+                                                  "grp_f32")],
+                         ids=["grp_mix", "grp_window", "grp_order", "grp_d512", "grp_max", "grp_f32"])
 def test_groups_bitwise_equal_single_calls(w):
     print(f"case {w.name} groups={w.groups}", flush=True)
     x = workloads.generate_groups(w)
