@@ -190,6 +190,24 @@ static inline hipError_t launch(const char* name, void (*kern)(KArgs...), dim3 g
 // 2^30 packed rows); returns a DUALKV_* status and the packed row count.
 int check_groups(const dualkv_group* groups, int32_t n, int64_t* rows);
 
+// Up to three GEMMs of one launch (gemm.hip).  Either the parts are column
+// ranges [lo[j], lo[j+1]) of the output that share A, each with its own B,
+// C and residual R (x Wk and x Wv side by side), or (ksplit) they are k
+// ranges that share C and R, C = R + sum_j A_j B_j accumulated in fp32 (the
+// input gradient of several projections of one input).  Part widths are
+// whole column tiles (256) or whole k tiles (64); the launcher of one GEMM
+// is the one-part case.
+constexpr int kMaxGemmParts = 3;
+struct GemmParts {
+  int n, ksplit;
+  int lo[kMaxGemmParts + 1];
+  const uint16_t* A[kMaxGemmParts];
+  const uint16_t* B[kMaxGemmParts];
+  uint16_t* C[kMaxGemmParts];
+  const uint16_t* R[kMaxGemmParts];
+  int64_t lda[kMaxGemmParts], ldb[kMaxGemmParts], ldc[kMaxGemmParts], ldr[kMaxGemmParts];
+};
+
 // ---- launchers implemented in the kernel translation units -------------
 hipError_t launch_repack(const void* src, void* dst, int64_t row_bytes, int N, int P, int R,
                          int direction, hipStream_t stream);

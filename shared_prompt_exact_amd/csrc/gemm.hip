@@ -13,11 +13,14 @@
 // waves and two slots), each wave 64 x 64 as 2 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16; K advances 64 at a time through an LDS ring
 // filled by direct global->LDS loads (the same swizzled tile layout as the
-// attention kernels).  Both
+// attention kernels).  When a k-major tile takes part (x W, x^T dy), both
 // operands number their k-slots in the order of the attention kernels'
 // transposed reads (half h of a 16-step holds k = 8*(j/4) + 4*h + j%4), so
-// k-major tiles are read transposed and m- or n-major tiles with two
-// 8-byte reads per operand.
+// k-major tiles are read transposed and an m-major tile with two 8-byte
+// reads per operand; when neither is k-major (dy W^T) both take k in
+// natural order, one 16-byte read per operand.  The wave forms C^T tiles
+// (B^T A^T), so each lane holds runs of four columns of one row of C and
+// the epilogue stores (and reads the residual) 8 bytes at a time.
 //
 // Bounds: rows of an [M][K] A tile or [N][K] B tile beyond M (N) re-read
 // the last valid row and their results are not stored.  Tiles whose rows
@@ -28,9 +31,11 @@
 #include "lds_tiles.h"
 
 namespace dualkv {
+
 namespace {
 
 constexpr int GBK = 64;
+constexpr int kWideBK = 64, kWideNS = 2;
 
 // Tile of BM x 64*WN: waves of 64 x 32*WN (WN = 2: BM = 128 with four waves,
 // a two-slot ring and two workgroups per CU, or BM = 256 with eight waves
@@ -41,8 +46,9 @@ template <int BM, int WN>
 struct GemmCfg {
   static constexpr int GBN = 64 * WN;             // columns of C per workgroup
   static constexpr int NW = BM / 32;              // waves, each 64 x 32*WN
-  static constexpr int NS = (BM == 256 && WN == 2) ? 3 : 2;    // ring slots
-  static constexpr int A_ELEMS = BM * GBK, B_ELEMS = GBN * GBK;
+  static constexpr int BK = WN == 4 ? kWideBK : GBK;   // k per ring slot
+  static constexpr int NS = WN == 4 ? kWideNS : (BM == 256 ? 3 : 2);    // ring slots
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = GBN * BK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
   static constexpr int LDS = NS * STAGE * 2;      // bytes
   static constexpr int ABLK = A_ELEMS * 2 / 1024, BBLK = B_ELEMS * 2 / 1024;   // 1-KiB blocks
@@ -52,10 +58,11 @@ struct GemmCfg {
 
 // A/B operand from an m- (or n-) major tile [rows][64 k]: row `row`,
 // 16-step ks, wave half hf, k-slots in the transposed-read order.
+template <int BK>
 __device__ __forceinline__ bf16x8 kslot_row_operand(const uint16_t* tile, int row, int ks, int hf) {
   const int c0 = 2 * ks, c1 = 2 * ks + 1;     // 16-byte chunks holding k = 16ks .. 16ks+15
-  const uint16_t* p0 = tile + row * GBK + ((c0 ^ swz<GBK>(row)) << 3) + 4 * hf;
-  const uint16_t* p1 = tile + row * GBK + ((c1 ^ swz<GBK>(row)) << 3) + 4 * hf;
+  const uint16_t* p0 = tile + row * BK + ((c0 ^ swz<BK>(row)) << 3) + 4 * hf;
+  const uint16_t* p1 = tile + row * BK + ((c1 ^ swz<BK>(row)) << 3) + 4 * hf;
   const uint2 a = *reinterpret_cast<const uint2*>(p0);
   const uint2 b = *reinterpret_cast<const uint2*>(p1);
   const uint4 u = {a.x, a.y, b.x, b.y};
@@ -64,32 +71,50 @@ __device__ __forceinline__ bf16x8 kslot_row_operand(const uint16_t* tile, int ro
 
 template <bool TA, bool TB, int BM, int WN>
 __global__ void __launch_bounds__(BM * 2)
-    gemm_bf16_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
-                     const uint16_t* __restrict__ B, int64_t ldb, uint16_t* C, int64_t ldc,
-                     const uint16_t* R, int64_t ldr, int tiles_n) {
+    gemm_bf16_kernel(int M, int N, int K, GemmParts P, int tiles_n, int vec) {
   using G = GemmCfg<BM, WN>;
-  constexpr int NS = G::NS, GBN = G::GBN;
+  constexpr int NS = G::NS, GBN = G::GBN, BK = G::BK;
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;     // 64 x 32*WN block of the wave
-  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
-  const int m0 = bm * BM, n0 = bn * GBN;
-  const int nk = (K + GBK - 1) / GBK;
+  int bm, bn;
+  gemm_tile_of(blockIdx.x, gridDim.x / tiles_n, tiles_n, bm, bn);
+  const int m0 = bm * BM;
+  // column part of this tile (all of C when the parts split k)
+  int cp = 0;
+  if (!P.ksplit)
+    while (cp + 1 < P.n && bn * GBN >= P.lo[cp + 1]) ++cp;
+  const int c_lo = P.ksplit ? 0 : P.lo[cp];
+  const int n0 = bn * GBN - c_lo;              // first column inside the part
+  const int Nl = P.ksplit ? N : P.lo[cp + 1] - c_lo;
+  const int nk = (K + BK - 1) / BK;
+
+  // operands of k tile t: its part, and the tile's first k inside the part
+  struct Ops { const uint16_t* A; int64_t lda; const uint16_t* B; int64_t ldb; int k0, Kl; };
+  auto ops = [&](int t) {
+    int kp = 0;
+    if (P.ksplit)
+      while (kp + 1 < P.n && t * BK >= P.lo[kp + 1]) ++kp;
+    const int k_lo = P.ksplit ? P.lo[kp] : 0;
+    const int bp = P.ksplit ? kp : cp;
+    return Ops{P.A[kp], P.lda[kp], P.B[bp], P.ldb[bp], t * BK - k_lo, P.ksplit ? P.lo[kp + 1] - k_lo : K};
+  };
 
   // this wave's share of the 1-KiB blocks of each tile
   auto issue = [&](int t) {
     uint16_t* As = lds + (t % NS) * G::STAGE;
     uint16_t* Bs = As + G::A_ELEMS;
-    const int k0 = t * GBK;
+    const Ops o = ops(t);
+    const int k0 = o.k0;
     if constexpr (TA)   // [K][M]: 64 rows of k, BM m each
-      dma_rows<BM>(A + (int64_t)k0 * lda + m0, lda, min(GBK, K - k0), As, wave * G::APW, G::APW, lane);
+      dma_rows<BM>(o.A + (int64_t)k0 * o.lda + m0, o.lda, min(BK, o.Kl - k0), As, wave * G::APW, G::APW, lane);
     else                // [M][K]: BM rows of m, 64 k each
-      dma_rows<GBK>(A + (int64_t)m0 * lda + k0, lda, min(BM, M - m0), As, wave * G::APW, G::APW, lane);
+      dma_rows<BK>(o.A + (int64_t)m0 * o.lda + k0, o.lda, min(BM, M - m0), As, wave * G::APW, G::APW, lane);
     if constexpr (TB)   // [N][K]
-      dma_rows<GBK>(B + (int64_t)n0 * ldb + k0, ldb, min(GBN, N - n0), Bs, wave * G::BPW, G::BPW, lane);
+      dma_rows<BK>(o.B + (int64_t)n0 * o.ldb + k0, o.ldb, min(GBN, Nl - n0), Bs, wave * G::BPW, G::BPW, lane);
     else                // [K][N]
-      dma_rows<GBN>(B + (int64_t)k0 * ldb + n0, ldb, min(GBK, K - k0), Bs, wave * G::BPW, G::BPW, lane);
+      dma_rows<GBN>(o.B + (int64_t)k0 * o.ldb + n0, o.ldb, min(BK, o.Kl - k0), Bs, wave * G::BPW, G::BPW, lane);
   };
 
   f32x16 acc[2][WN];
@@ -106,18 +131,19 @@ __global__ void __launch_bounds__(BM * 2)
   for (int t = 0; t < nk; ++t) {
     // tile t has landed once only the later tiles' loads (up to NS-2 of
     // them, APW + BPW instructions each) are pending
-    if (NS == 3 && t + 1 < nk) wait_vmcnt<(NS - 2) * (G::APW + G::BPW)>();
+    if (NS >= 3 && t + NS - 2 < nk) wait_vmcnt<(NS >= 3 ? NS - 2 : 0) * (G::APW + G::BPW)>();
     else wait_vmcnt<0>();
     block_sync();                              // everyone's; slot (t-1)%NS is free
     if (t + NS - 1 < nk) issue(t + NS - 1);
     uint16_t* As = lds + (t % NS) * G::STAGE;
     uint16_t* Bs = As + G::A_ELEMS;
     if constexpr (TA && !TB) {
-      const int kv = K - t * GBK;              // valid k rows of this tile
-      if (kv < GBK) {
+      const Ops o = ops(t);
+      const int kv = o.Kl - o.k0;             // valid k rows of this tile
+      if (kv < BK) {
         // rows kv..63 of both k-major tiles re-read row kv-1: zero them
         constexpr int CA = BM / 8, CB = GBN / 8;   // 16-byte chunks per row
-        for (int i = tid; i < (GBK - kv) * (CA + CB); i += BM * 2) {
+        for (int i = tid; i < (BK - kv) * (CA + CB); i += BM * 2) {
           const int r = kv + i / (CA + CB), c = i % (CA + CB);
           if (c < CA) *reinterpret_cast<uint4*>(As + r * BM + c * 8) = uint4{0, 0, 0, 0};
           else *reinterpret_cast<uint4*>(Bs + r * GBN + (c - CA) * 8) = uint4{0, 0, 0, 0};
@@ -126,57 +152,84 @@ __global__ void __launch_bounds__(BM * 2)
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 a[2], b[WN];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int mr = wm * 64 + i * 32;
         if constexpr (TA) a[i] = trans_operand<BM>(As, 0, mr, ks, lane);
-        else a[i] = kslot_row_operand(As, mr + l32, ks, hf);
+        else if constexpr (TB) a[i] = row_operand<BK>(As, mr + l32, ks, hf);
+        else a[i] = kslot_row_operand<BK>(As, mr + l32, ks, hf);
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const int nr = wn * 32 * WN + j * 32;
-        if constexpr (TB) b[j] = kslot_row_operand(Bs, nr + l32, ks, hf);
+        if constexpr (TB) b[j] = row_operand<BK>(Bs, nr + l32, ks, hf);
         else b[j] = trans_operand<GBN>(Bs, 0, nr, ks, lane);
       }
+      // the product is formed transposed (C^T tile = B^T A^T), so that a
+      // lane holds four consecutive columns of C in each register group
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
     }
   }
 
-  // C tile (i, j): lane column n, rows 8*(e/4) + 4*hf + e%4
+  // C^T tile (i, j): lane row m, columns 8*(e/4) + 4*hf + e%4; four
+  // consecutive columns go out (and the residual comes in) as 8 bytes
+  uint16_t* C = P.C[cp];
+  const uint16_t* R = P.R[cp];
+  const int64_t ldc = P.ldc[cp], ldr = P.ldr[cp];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + i * 32 + l32;
+    if (m >= M) continue;
+    uint16_t* crow = C + (int64_t)m * ldc;
+    const uint16_t* rrow = R ? R + (int64_t)m * ldr : nullptr;
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int n = n0 + wn * 32 * WN + j * 32 + l32;
-      if (n >= N) continue;
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
-        if (m < M) {
-          float x = acc[i][j][e];
-          if (R) x += bf16_to_f32(R[(int64_t)m * ldr + n]);
-          C[(int64_t)m * ldc + n] = f32_to_bf16(x);
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 32 * WN + j * 32 + 8 * q + 4 * hf;   // column inside the part
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[i][j][4 * q + e];
+        if (vec && n + 3 < Nl) {
+          if (rrow) {
+            const uint2 r = *reinterpret_cast<const uint2*>(rrow + n);
+            x[0] += __uint_as_float(r.x << 16);
+            x[1] += __uint_as_float(r.x & 0xffff0000u);
+            x[2] += __uint_as_float(r.y << 16);
+            x[3] += __uint_as_float(r.y & 0xffff0000u);
+          }
+          uint2 o;
+          o.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+          o.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+          *reinterpret_cast<uint2*>(crow + n) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < Nl) crow[n + e] = f32_to_bf16(x[e] + (rrow ? bf16_to_f32(rrow[n + e]) : 0.f));
         }
       }
-    }
+  }
 }
 
 template <bool TA, bool TB, int BM, int WN>
-hipError_t run_gemm(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                    int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
+hipError_t run_gemm(int M, int N, int K, const GemmParts& P, hipStream_t stream) {
   using G = GemmCfg<BM, WN>;
   static_assert(G::LDS <= 160 * 1024, "LDS budget");
   static const hipError_t attr = allow_lds(gemm_bf16_kernel<TA, TB, BM, WN>, G::LDS);
   if (attr != hipSuccess) return attr;
   const int tm = (M + BM - 1) / BM, tn = (N + G::GBN - 1) / G::GBN;
+  // 8-byte epilogue accesses need 8-byte aligned rows of every C (and R)
+  int vec = 1;
+  for (int j = 0; j < (P.ksplit ? 1 : P.n); ++j)
+    vec &= P.ldc[j] % 4 == 0 && reinterpret_cast<uintptr_t>(P.C[j]) % 8 == 0 &&
+           (!P.R[j] || (P.ldr[j] % 4 == 0 && reinterpret_cast<uintptr_t>(P.R[j]) % 8 == 0));
   return launch("gemm", gemm_bf16_kernel<TA, TB, BM, WN>, dim3((unsigned)(tm * tn)), dim3(BM * 2), G::LDS, stream, M,
-                N, K, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb,
-                static_cast<uint16_t*>(C), ldc, static_cast<const uint16_t*>(R), ldr, tn);
+                N, K, P, tn, vec);
 }
 
 constexpr int GBN = 128;   // the narrowest tile's columns: the shape rules below
@@ -212,22 +265,39 @@ int gemm_shape_ok(bool ta, bool tb, int M, int N, int K, int64_t lda, int64_t ld
   return 1;
 }
 
-hipError_t launch_gemm(bool ta, bool tb, int M, int N, int K, const void* A, int64_t lda, const void* B,
-                       int64_t ldb, void* C, int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
+hipError_t launch_gemm_parts(bool ta, bool tb, int M, int N, int K, const GemmParts& P, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (ta && tb) return hipErrorInvalidValue;
   const bool tall = use_tall(ta, M, N), wide = use_wide(ta, M, N);
   if (ta)
-    return wide ? run_gemm<true, false, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-         : tall ? run_gemm<true, false, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-                : run_gemm<true, false, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+    return wide ? run_gemm<true, false, 256, 4>(M, N, K, P, stream)
+         : tall ? run_gemm<true, false, 256, 2>(M, N, K, P, stream)
+                : run_gemm<true, false, 128, 2>(M, N, K, P, stream);
   if (tb)
-    return wide ? run_gemm<false, true, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-         : tall ? run_gemm<false, true, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-                : run_gemm<false, true, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
-  return wide ? run_gemm<false, false, 256, 4>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-       : tall ? run_gemm<false, false, 256, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream)
-              : run_gemm<false, false, 128, 2>(M, N, K, A, lda, B, ldb, C, ldc, R, ldr, stream);
+    return wide ? run_gemm<false, true, 256, 4>(M, N, K, P, stream)
+         : tall ? run_gemm<false, true, 256, 2>(M, N, K, P, stream)
+                : run_gemm<false, true, 128, 2>(M, N, K, P, stream);
+  return wide ? run_gemm<false, false, 256, 4>(M, N, K, P, stream)
+       : tall ? run_gemm<false, false, 256, 2>(M, N, K, P, stream)
+              : run_gemm<false, false, 128, 2>(M, N, K, P, stream);
+}
+
+hipError_t launch_gemm(bool ta, bool tb, int M, int N, int K, const void* A, int64_t lda, const void* B,
+                       int64_t ldb, void* C, int64_t ldc, const void* R, int64_t ldr, hipStream_t stream) {
+  GemmParts P{};
+  P.n = 1;
+  P.ksplit = 0;
+  P.lo[0] = 0;
+  P.lo[1] = N;
+  P.A[0] = static_cast<const uint16_t*>(A);
+  P.lda[0] = lda;
+  P.B[0] = static_cast<const uint16_t*>(B);
+  P.ldb[0] = ldb;
+  P.C[0] = static_cast<uint16_t*>(C);
+  P.ldc[0] = ldc;
+  P.R[0] = static_cast<const uint16_t*>(R);
+  P.ldr[0] = ldr;
+  return launch_gemm_parts(ta, tb, M, N, K, P, stream);
 }
 
 }  // namespace dualkv

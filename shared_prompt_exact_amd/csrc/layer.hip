@@ -25,6 +25,7 @@ namespace dualkv {
 hipError_t launch_gemm(bool ta, bool tb, int M, int N, int K, const void* A, int64_t lda, const void* B,
                        int64_t ldb, void* C, int64_t ldc, const void* R, int64_t ldr, hipStream_t stream);
 int gemm_shape_ok(bool ta, bool tb, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc);
+hipError_t launch_gemm_parts(bool ta, bool tb, int M, int N, int K, const GemmParts& P, hipStream_t stream);
 hipError_t launch_rmsnorm_fwd(int T, int H, float eps, const void* x, const void* w, void* y, float* rstd,
                               hipStream_t s);
 hipError_t launch_rmsnorm_bwd(int T, int H, const void* x, const void* w, const float* rstd, const void* dy,
@@ -38,6 +39,67 @@ hipError_t launch_swiglu_bwd(int64_t n, const void* u, const void* g, const void
 namespace {
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// op(A) Ba -> Ca and op(A) Bb -> Cb (same A, B row-major [K][N*], C [M][N*]):
+// one launch with two column parts when both widths are whole 256-column
+// tiles, else two launches.
+hipError_t gemm_cols2(bool ta, int M, int Na, int Nb, int K, const void* A, int64_t lda, const void* Ba,
+                      const void* Bb, void* Ca, void* Cb, hipStream_t s) {
+  if (Na % 256 != 0 || Nb % 256 != 0) {
+    hipError_t e = launch_gemm(ta, false, M, Na, K, A, lda, Ba, Na, Ca, Na, nullptr, 0, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm(ta, false, M, Nb, K, A, lda, Bb, Nb, Cb, Nb, nullptr, 0, s);
+  }
+  GemmParts P{};
+  P.n = 2;
+  P.ksplit = 0;
+  P.lo[0] = 0;
+  P.lo[1] = Na;
+  P.lo[2] = Na + Nb;
+  P.A[0] = P.A[1] = static_cast<const uint16_t*>(A);
+  P.lda[0] = P.lda[1] = lda;
+  P.B[0] = static_cast<const uint16_t*>(Ba);
+  P.B[1] = static_cast<const uint16_t*>(Bb);
+  P.ldb[0] = Na;
+  P.ldb[1] = Nb;
+  P.C[0] = static_cast<uint16_t*>(Ca);
+  P.C[1] = static_cast<uint16_t*>(Cb);
+  P.ldc[0] = Na;
+  P.ldc[1] = Nb;
+  return launch_gemm_parts(ta, false, M, Na + Nb, K, P, s);
+}
+
+// C [M][N] = sum_j A_j B_j^T with A_j [M][K_j] and B_j [N][K_j] (the input
+// gradient of several projections of one input): one launch over k parts
+// when every K_j is whole 64-k tiles, else one launch per part, each adding
+// the previous result as its residual.
+hipError_t gemm_ksum(int M, int N, int np, const int* Ks, const void* const* As, const void* const* Bs, void* C,
+                     hipStream_t s) {
+  bool whole = np <= kMaxGemmParts;
+  for (int j = 0; j < np; ++j) whole = whole && Ks[j] % 64 == 0;
+  if (!whole) {
+    for (int j = 0; j < np; ++j) {
+      hipError_t e = launch_gemm(false, true, M, N, Ks[j], As[j], Ks[j], Bs[j], Ks[j], C, N, j ? C : nullptr,
+                                 j ? N : 0, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GemmParts P{};
+  P.n = np;
+  P.ksplit = 1;
+  P.lo[0] = 0;
+  for (int j = 0; j < np; ++j) {
+    P.lo[j + 1] = P.lo[j] + Ks[j];
+    P.A[j] = static_cast<const uint16_t*>(As[j]);
+    P.lda[j] = Ks[j];
+    P.B[j] = static_cast<const uint16_t*>(Bs[j]);
+    P.ldb[j] = Ks[j];
+  }
+  P.C[0] = static_cast<uint16_t*>(C);
+  P.ldc[0] = N;
+  return launch_gemm_parts(false, true, M, N, P.lo[np], P, s);
+}
 
 struct LayerShape {
   int T, Hm, Hq, Hkv, D, F;
@@ -288,8 +350,7 @@ int dualkv_layer_fwd(const dualkv_layer_params* lp, const dualkv_group* groups, 
   if ((e = (call)) != hipSuccess) return status_of(e)
   DKV_TRY(launch_rmsnorm_fwd(T, Hm, lp->norm_eps, x, wt->norm1, v.h1, v.rstd1, hs));
   DKV_TRY(launch_gemm(false, false, T, QD, Hm, v.h1, Hm, wt->wq, QD, v.q, QD, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(false, false, T, KD, Hm, v.h1, Hm, wt->wk, KD, v.k, KD, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(false, false, T, KD, Hm, v.h1, Hm, wt->wv, KD, v.v, KD, nullptr, 0, hs));
+  DKV_TRY(gemm_cols2(false, T, KD, KD, Hm, v.h1, Hm, wt->wk, wt->wv, v.k, v.v, hs));
   DKV_TRY(launch_rope(T, s.Hq, s.D, G, lp->rope_base, 0, v.q, hs));
   DKV_TRY(launch_rope(T, s.Hkv, s.D, G, lp->rope_base, 0, v.k, hs));
   st = dualkv_fwd_groups(&ap, groups, n_groups, v.q, v.k, v.v, v.o, v.lse, stream);
@@ -333,8 +394,12 @@ int dualkv_layer_bwd(const dualkv_layer_params* lp, const dualkv_group* groups, 
   DKV_TRY(launch_gemm(false, true, T, F, Hm, dy, Hm, wt->w2, Hm, w.dm, F, nullptr, 0, hs));
   DKV_TRY(launch_gemm(true, false, F, Hm, T, v.m, F, dy, Hm, gr->w2, Hm, nullptr, 0, hs));
   DKV_TRY(launch_swiglu_bwd((int64_t)T * F, v.u, v.g, w.dm, w.du, w.dg, hs));
-  DKV_TRY(launch_gemm(false, true, T, Hm, F, w.du, F, wt->w1, F, w.dh2, Hm, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(false, true, T, Hm, F, w.dg, F, wt->w3, F, w.dh2, Hm, w.dh2, Hm, hs));
+  {
+    const int Ks[] = {F, F};
+    const void* As[] = {w.du, w.dg};
+    const void* Bs[] = {wt->w1, wt->w3};
+    DKV_TRY(gemm_ksum(T, Hm, 2, Ks, As, Bs, w.dh2, hs));
+  }
   DKV_TRY(launch_gemm(true, false, Hm, F, T, v.h2, Hm, w.du, F, gr->w1, F, nullptr, 0, hs));
   DKV_TRY(launch_gemm(true, false, Hm, F, T, v.h2, Hm, w.dg, F, gr->w3, F, nullptr, 0, hs));
   // h2 = RMSNorm(x1); the residual passes dy on to x1
@@ -347,12 +412,14 @@ int dualkv_layer_bwd(const dualkv_layer_params* lp, const dualkv_group* groups, 
   if (st != DUALKV_OK) return st;
   DKV_TRY(launch_rope(T, s.Hq, s.D, G, lp->rope_base, 1, w.dq, hs));
   DKV_TRY(launch_rope(T, s.Hkv, s.D, G, lp->rope_base, 1, w.dk, hs));
-  DKV_TRY(launch_gemm(false, true, T, Hm, QD, w.dq, QD, wt->wq, QD, w.dh1, Hm, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(false, true, T, Hm, KD, w.dk, KD, wt->wk, KD, w.dh1, Hm, w.dh1, Hm, hs));
-  DKV_TRY(launch_gemm(false, true, T, Hm, KD, w.dv, KD, wt->wv, KD, w.dh1, Hm, w.dh1, Hm, hs));
+  {
+    const int Ks[] = {QD, KD, KD};
+    const void* As[] = {w.dq, w.dk, w.dv};
+    const void* Bs[] = {wt->wq, wt->wk, wt->wv};
+    DKV_TRY(gemm_ksum(T, Hm, 3, Ks, As, Bs, w.dh1, hs));
+  }
   DKV_TRY(launch_gemm(true, false, Hm, QD, T, v.h1, Hm, w.dq, QD, gr->wq, QD, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(true, false, Hm, KD, T, v.h1, Hm, w.dk, KD, gr->wk, KD, nullptr, 0, hs));
-  DKV_TRY(launch_gemm(true, false, Hm, KD, T, v.h1, Hm, w.dv, KD, gr->wv, KD, nullptr, 0, hs));
+  DKV_TRY(gemm_cols2(true, Hm, KD, KD, T, v.h1, Hm, w.dk, w.dv, gr->wk, gr->wv, hs));
   DKV_TRY(launch_rmsnorm_bwd(T, Hm, x, wt->norm1, v.rstd1, w.dh1, w.dx1, dx, gr->norm1, w.part, hs));
 #undef DKV_TRY
   return DUALKV_OK;

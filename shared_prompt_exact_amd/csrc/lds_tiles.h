@@ -10,7 +10,8 @@
 //    rows at one logical chunk): swz takes 16 distinct values over 16
 //    consecutive rows (D >= 128; rows are 256 B or more, so the position is
 //    the chunk index mod 16), or 8 distinct values over the 8 rows of each
-//    parity (D = 64: two 128-byte rows per 256 bytes);
+//    parity (D = 64: two 128-byte rows per 256 bytes), or 4 over the 4 rows
+//    of each residue mod 4 (D = 32: four 64-byte rows per 256 bytes);
 //  * transposed operands (ds_read_b64_tr_b16, 32 lanes per clock = 4
 //    consecutive rows x 4 consecutive chunks): the 4 rows differ in swz
 //    bits 2-3 (D = 64: the two rows of each parity differ in bit 2), the 4
@@ -37,7 +38,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  if constexpr (D == 32) return (row >> 2) & 3;
+  else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   else return ((row & 3) << 2) | ((row >> 2) & 3);
 }
 

@@ -68,6 +68,27 @@ __device__ __forceinline__ int balanced_block(int bid, int units, int per_unit) 
   return bid;
 }
 
+// GEMM tile of workgroup `bid` on a tm x tn grid of C tiles.  The grid is
+// cut into blocks of 4 x 8 (or 8 x 4) tiles, numbered row by row; XCD x
+// (the workgroups bid = x mod 8) walks the x-th eighth of that numbering,
+// so the 32 workgroups it runs at a time (one per CU) are one block and
+// its L2 sees 12 distinct operand panels per k-step instead of the 18 of a
+// row-major walk.  Grids that do not split into such blocks stay row-major.
+__device__ __forceinline__ void gemm_tile_of(int bid, int tm, int tn, int& bm, int& bn) {
+  constexpr int X = 8, PER = 32;
+  const int sn = tn % 8 == 0 ? 8 : 4, sm = PER / sn;
+  if (tn % sn != 0 || tm % sm != 0) {
+    bm = bid / tn;
+    bn = bid % tn;
+    return;
+  }
+  const int q = (bid % X) * (tm * tn / X) + bid / X;   // position in block order
+  const int blk = q / PER, in = q % PER;
+  const int bpr = tn / sn;                             // blocks per block row
+  bm = (blk / bpr) * sm + in / sn;
+  bn = (blk % bpr) * sn + in % sn;
+}
+
 // Grid size for balanced_block.
 inline int64_t balanced_grid(int units, int64_t per_unit) {
   constexpr int X = 8;

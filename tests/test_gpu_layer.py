@@ -52,6 +52,8 @@ def tight(name, got, want, rel=2e-3):
     # 256 x 256 tiles (256-wide column blocks, at least one block per CU), a ragged last row block
     # and, in the weight-gradient form, a ragged k
     (0, 0, 4000, 4096, 192, True), (0, 1, 4096, 4096, 128, False), (1, 0, 4096, 4096, 1001, False),
+    # rows of C not 8-byte aligned (element-wise epilogue) and a ragged last column block
+    (0, 1, 300, 383, 256, True), (0, 1, 4096, 4096, 256, True),
 ])
 def test_gemm(ta, tb, M, N, K, res):
     print(f"gemm ta={ta} tb={tb} M={M} N={N} K={K} residual={res}", flush=True)
@@ -108,10 +110,18 @@ Hm, Hq, Hkv, D, F = 256, 4, 2, 64, 384
 LAYER_CASES = [
     ([(2, 70, 45), (3, 40, 30)], 0, [45, 20, 30, 0, 17]),
     ([(3, 100, 60)], 48, None),
+    # K/V projection widths of whole 256-column tiles: x Wk and x Wv (and
+    # their weight gradients) run as one two-part launch
+    ([(2, 90, 50)], 0, None, (8, 4, 64)),
 ]
 
 
-def layer_inputs(groups, seed):
+def case_shape(case):
+    """(Hq, Hkv, D) of a layer case; the module defaults unless it names its own."""
+    return LAYER_CASES[case][3] if len(LAYER_CASES[case]) > 3 else (Hq, Hkv, D)
+
+
+def layer_inputs(groups, seed, Hq=Hq, Hkv=Hkv, D=D):
     rng = np.random.default_rng(seed)
     T = sum(P + N * R for N, P, R in groups)
     sh = {"norm1": (Hm,), "wq": (Hm, Hq * D), "wk": (Hm, Hkv * D), "wv": (Hm, Hkv * D), "wo": (Hq * D, Hm),
@@ -123,7 +133,7 @@ def layer_inputs(groups, seed):
     return rounded(rng, T, Hm), rounded(rng, T, Hm), W
 
 
-def run_layer(groups, window, vl, x, dy, W):
+def run_layer(groups, window, vl, x, dy, W, Hq=Hq, Hkv=Hkv, D=D):
     valid = None if vl is None else torch.tensor(vl, dtype=torch.int32, device="cuda")
     p = dk.make_layer_params(Hm, Hq, Hkv, D, F, window, 1e4, 1e-6, valid)
     Wd = {n: bf(W[n]) for n in dk.LAYER_WEIGHTS}
@@ -136,22 +146,25 @@ def run_layer(groups, window, vl, x, dy, W):
 
 @pytest.mark.parametrize("case", range(len(LAYER_CASES)))
 def test_layer_matches_oracle(case):
-    groups, window, vl = LAYER_CASES[case]
-    print(f"layer groups={groups} window={window} valid={vl}", flush=True)
-    x, dy, W = layer_inputs(groups, 20 + case)
-    y, dx, grads = run_layer(groups, window, vl, x, dy, W)
-    ref = ol.layer_fold(x, W, dy, groups, Hq, Hkv, window, 1e4, 1e-6, vl)
+    groups, window, vl = LAYER_CASES[case][:3]
+    hq, hkv, d = case_shape(case)
+    print(f"layer groups={groups} window={window} valid={vl} heads={hq}/{hkv} D={d}", flush=True)
+    x, dy, W = layer_inputs(groups, 20 + case, hq, hkv, d)
+    y, dx, grads = run_layer(groups, window, vl, x, dy, W, hq, hkv, d)
+    ref = ol.layer_fold(x, W, dy, groups, hq, hkv, window, 1e4, 1e-6, vl)
     out = {"y": check("y", host(y), ref["y"], "bf16", False), "dx": check("dx", host(dx), ref["dx"], "bf16", False)}
     for n in dk.LAYER_WEIGHTS:
         out[n] = check(n, host(grads[n]), ref["grads"][n], "bf16", False)
     print({k: f"{v[0]:.2e}" for k, v in out.items()}, flush=True)
 
 
-def test_layer_bitwise_reproducible():
-    groups, window, vl = LAYER_CASES[0]
-    x, dy, W = layer_inputs(groups, 30)
-    a = run_layer(groups, window, vl, x, dy, W)
-    b = run_layer(groups, window, vl, x, dy, W)
+@pytest.mark.parametrize("case", [0, 2])
+def test_layer_bitwise_reproducible(case):
+    groups, window, vl = LAYER_CASES[case][:3]
+    hq, hkv, d = case_shape(case)
+    x, dy, W = layer_inputs(groups, 30, hq, hkv, d)
+    a = run_layer(groups, window, vl, x, dy, W, hq, hkv, d)
+    b = run_layer(groups, window, vl, x, dy, W, hq, hkv, d)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     for n in dk.LAYER_WEIGHTS:
         assert torch.equal(a[2][n], b[2][n]), n
