@@ -348,8 +348,12 @@ __global__ void __launch_bounds__(NW * 64)
     }
   }
 
-  if (my_r < b.seglen) {
-    uint16_t* orow = dq + qrow * ostride + (int64_t)h * D;
+  // the row and half of this lane are formed again from the lane index
+  // (mbcnt) rather than kept in registers across the tile loop
+  const int ln = __lane_id();
+  const int e_r = wr0 + (ln & 31), e_hf = ln >> 5;
+  if (e_r < b.seglen) {
+    uint16_t* orow = dq + ((int64_t)b.base + e_r) * ostride + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DBH; ++db)
 #pragma unroll
@@ -357,7 +361,7 @@ __global__ void __launch_bounds__(NW * 64)
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
-        *reinterpret_cast<uint2*>(orow + (dh * DBH + db) * 32 + 8 * g4 + 4 * hf) = pk.u;
+        *reinterpret_cast<uint2*>(orow + (dh * DBH + db) * 32 + 8 * g4 + 4 * e_hf) = pk.u;
       }
   }
 }
