@@ -424,7 +424,12 @@ def main():
         rstep()
         ms_rep = timed(rstep, rsteps, torch)
         ms_rep_fwd = timed(rfwd, rsteps, torch)
+        dk.dualkv_profile_start()
+        for _ in range(rsteps):
+            rstep()
+        rprof = dk.dualkv_profile_stop()
         rep = {"ms_fwd_bwd": round(ms_rep, 3), "ms_fwd": round(ms_rep_fwd, 3),
+               "kernels_avg_ms": {name: round(ms / n, 4) for name, (n, ms) in rprof.items()},
                "tflops_fwd_bwd": round(14 * rep_pairs * Hq * D / (ms_rep * 1e-3) / 1e12, 2),
                "speedup_fwd_bwd": round(ms_rep / (ms_fwd + ms_bwd), 3),
                "speedup_fwd": round(ms_rep_fwd / ms_fwd, 3),

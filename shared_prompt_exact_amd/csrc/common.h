@@ -85,7 +85,8 @@ LaunchOrder make_order(const int64_t* count, int ngroups, Cost cost) {
   struct Chunk { double cost; int g, loc, len; };
   Chunk ch[kMaxChunks];
   int nc = 0;
-  const int per = ngroups > 0 ? kMaxChunks / ngroups : 1;
+  // one group: a single chunk, the group's own order
+  const int per = ngroups > 1 ? kMaxChunks / ngroups : 1;
   for (int i = 0; i < ngroups; ++i) {
     const int64_t m = count[i];
     const int64_t k = m < per ? m : per;
