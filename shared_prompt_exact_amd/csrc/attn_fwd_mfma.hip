@@ -44,352 +44,21 @@ template <int V>
 struct IntC {
   static constexpr int value = V;
 };
-// Ring slot of a tile: a compile-time constant (IntC) on the unrolled path,
-// a runtime value otherwise.
-template <int V>
-__device__ __forceinline__ constexpr int slot_value(IntC<V>) { return V; }
-__device__ __forceinline__ int slot_value(int x) { return x; }
 
-template <int D, int BN, int NW, int NS, int DS>
-struct FwdCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int K_ELEMS = BN * D;            // swizzled row-major K tile
-  static constexpr int V_ELEMS = BN * D;            // swizzled row-major V tile
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;   // elements per ring slot
-  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * 16 * 4 : 0;   // partial-score exchange
-  static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
-  static constexpr int KBLK = BN * D * 2 / 1024;    // 1 KiB blocks per K (or V) tile
-  static constexpr int BPW = KBLK / NW;             // blocks per wave per tile, for K and V each
-  static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
-};
-
-// DS > 1 splits the head dim over DS consecutive waves (they own the same
-// 32 query rows, each a 1/DS slice of D for Q^T, the K contraction and the O
-// accumulator); their partial scores meet in LDS and every one of them adds
-// the DS partials in head-dim order, so they agree bit for bit.
-template <int D, int BN, int NW, int NS, int DS>
-__global__ void __launch_bounds__(NW * 64)
-    fwd_mfma_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
-                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                    uint16_t* __restrict__ o, float* __restrict__ lse) {
-  using C = FwdCfg<D, BN, NW, NS, DS>;
-  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
-  constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
-  extern __shared__ __align__(16) uint16_t lds[];
-
-  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dh = wave % DS, wq = wave / DS;     // head-dim half, query slot
-  const int BM = 32 * NWQ / HG;
-  const int NB = GB.off[G.n];                   // row blocks of all groups, per head group
-  const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
-  if (L < 0) return;                            // grid padding (whole workgroup)
-  const int hgi = L / NB;
-  // the prompt group of this block; rows and statistics below are the group's
-  int blk;
-  const int gi = order_lookup(GB.ord, L % NB, blk);
-  const int nbP = GB.nbP[gi], nbR = GB.nbR[gi];
-  const Problem pr = group_problem(pa, G, gi);
-  {
-    const int64_t r0 = G.row0[gi];
-    q += r0 * pr.Hq * D;
-    o += r0 * pr.Hq * D;
-    k += r0 * pr.Hkv * D;
-    v += r0 * pr.Hkv * D;
-    lse += r0;
-  }
-  const int gpw = pr.g / HG;
-  const int c = hgi / gpw;
-  const int h = c * pr.g + (hgi % gpw) * HG + wq % HG;
-  const RowBlock b = decode_block(pr, blk, BM, nbP, nbR);
-
-  const int wr0 = b.r0 + (wq / HG) * 32;        // first row of this wave
-  const int my_r = wr0 + l32;
-  const bool qvalid = my_r < b.nvalid;
-  const int qpos = b.posoff + my_r;
-  const int64_t qrow = (int64_t)b.base + my_r;
-  const int64_t ostride = (int64_t)pr.Hq * D;
-
-  const int blk_hi = min(b.r0 + BM, b.nvalid) - 1;   // last valid row of the block
-  const int w_hi = min(wr0 + 31, b.nvalid - 1);
-  const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
-  const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
-
-  // Q^T as B operands, one per 16-wide head-dim step of this wave's dims.
-  bf16x8 qB[KTH];
-#pragma unroll
-  for (int kk = 0; kk < KTH; ++kk) {
-    uint4 z = {0, 0, 0, 0};
-    if (qvalid)
-      z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * (dh * KTH + kk) + 8 * hf);
-    qB[kk] = __builtin_bit_cast(bf16x8, z);
-  }
-  // Q must be in registers before the key loop: the loop's own waits only
-  // count the tile loads, so drain it here (known to the compiler).
-  wait_vmcnt<0>();
-  asm volatile("" ::: "memory");
-
-  f32x16 acc[DBH];
-#pragma unroll
-  for (int db = 0; db < DBH; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  float* const xch = reinterpret_cast<float*>(lds + NS * C::STAGE);   // DS > 1 only
-  const float c2 = pr.scale * kLog2e;
-  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;   // visible distance bound
-
-  if (blk_hi >= b.r0) {
-    const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
-    const int ntiles = tr.nA + tr.nB;
-    const int64_t rs = (int64_t)pr.Hkv * D;
-    // Ring of NS slots fed by direct global->LDS loads, NS-1 tiles ahead.
-    auto issue = [&](int t) {
-      const KeyTile kt = tile_at(pr, b, tr, t, BN);
-      const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
-      uint16_t* slot = lds + (t % NS) * C::STAGE;
-      const int nv = min(BN, kt.lim);
-      dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
-      dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
-    };
-#pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-      if (t < ntiles) issue(t);
-
-    // One key tile.  Where the loop below is unrolled by NS the ring slot is
-    // a compile-time constant, so every LDS operand address is a per-lane
-    // base plus an immediate offset.
-    auto step = [&](int it, auto slot_c) {
-      const int SLOT = slot_value(slot_c);
-      // Tile `it` has landed once at most the loads of later issued tiles
-      // (up to NS-2 of them, 2*BPW instructions each) are pending.
-      if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
-      else wait_vmcnt<0>();
-      block_sync();
-      if (it + NS - 1 < ntiles) issue(it + NS - 1);
-
-      const KeyTile kt = tile_at(pr, b, tr, it, BN);
-      const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
-      const uint16_t* Ks = lds + SLOT * C::STAGE;
-      const uint16_t* Vs = Ks + C::K_ELEMS;
-      f32x16 s[NB32];
-#pragma unroll
-      for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      if (kind != 0) {
-        if constexpr (KTH <= 8 && DS != 2) {
-          // the K operands of k-step kk+1 are read before the MFMAs of step
-          // kk (scheduling fences keep them there), so their LDS latency
-          // overlaps MFMA work (measured slower with the two-way head-dim
-          // split, which keeps the compiler's order)
-          bf16x8 ka[NB32];
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb) ka[kb] = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
-#pragma unroll
-          for (int kk = 0; kk < KTH; ++kk) {
-            bf16x8 kn[NB32];
-#pragma unroll
-            for (int kb = 0; kb < NB32; ++kb) kn[kb] = ka[kb];
-            if (kk + 1 < KTH) {
-#pragma unroll
-              for (int kb = 0; kb < NB32; ++kb) kn[kb] = row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk + 1, hf);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NB32; ++kb) s[kb] = mfma32(ka[kb], qB[kk], s[kb]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kb = 0; kb < NB32; ++kb) ka[kb] = kn[kb];
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < KTH; ++kk) {
-#pragma unroll
-            for (int kb = 0; kb < NB32; ++kb)
-              s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s[kb]);
-            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      if constexpr (DS > 1) {
-        // partial scores of the two halves meet in LDS (all waves pass the
-        // barrier; both members of a pair have the same `kind`)
-        // layout [wave][float4 j][lane]: each 16-byte store or load of a wave
-        // covers 1 KiB contiguous (no bank conflicts)
-        float4* const x4 = reinterpret_cast<float4*>(xch);
-        if (kind != 0)
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-              x4[(wave * 4 * NB32 + 4 * kb + i4) * 64 + lane] =
-                  make_float4(s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]);
-        block_sync();
-        if (kind != 0)
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              if constexpr (DS == 2) {
-                const float4 t = x4[((wave ^ 1) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
-                // lower half first in both waves: identical sums
-                s[kb][4 * i4 + 0] = dh == 0 ? s[kb][4 * i4 + 0] + t.x : t.x + s[kb][4 * i4 + 0];
-                s[kb][4 * i4 + 1] = dh == 0 ? s[kb][4 * i4 + 1] + t.y : t.y + s[kb][4 * i4 + 1];
-                s[kb][4 * i4 + 2] = dh == 0 ? s[kb][4 * i4 + 2] + t.z : t.z + s[kb][4 * i4 + 2];
-                s[kb][4 * i4 + 3] = dh == 0 ? s[kb][4 * i4 + 3] + t.w : t.w + s[kb][4 * i4 + 3];
-                continue;
-              }
-              // the DS partials, this wave's own included, read back and added
-              // in head-dim order by every wave: identical sums in all of them
-              float4 t = x4[((wave - dh) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
-#pragma unroll
-              for (int pp = 1; pp < DS; ++pp) {
-                const float4 v4 = x4[((wave - dh + pp) * 4 * NB32 + 4 * kb + i4) * 64 + lane];
-                t.x += v4.x; t.y += v4.y; t.z += v4.z; t.w += v4.w;
-              }
-              s[kb][4 * i4 + 0] = t.x;
-              s[kb][4 * i4 + 1] = t.y;
-              s[kb][4 * i4 + 2] = t.z;
-              s[kb][4 * i4 + 3] = t.w;
-            }
-      }
-      if (kind != 0) {
-        if (kind == 2) {
-          // Branch-free mask: key kc (+4*hf) is visible iff
-          // 0 <= qpos - pos < window (one unsigned compare) and kc < lim.
-          const int d0 = qpos - kt.pos0 - 4 * hf;
-          const int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
-#pragma unroll
-          for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kc = kb * 32 + 8 * (i >> 2) + (i & 3);
-              const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
-              s[kb][i] = vis ? s[kb][i] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, swap_halves(mx));
-        // The running max m only moves when the tile's max exceeds it by
-        // more than kRescale (log2 units): the softmax is the same for any
-        // reference value (numerator and denominator share it), p stays
-        // below 2^kRescale, and the O rescale -- a multiply per accumulator
-        // register -- becomes rare instead of happening on most tiles.
-        const bool grow = mx * c2 > m + kRescale;
-        if (__any(grow)) {
-          const float mnew = grow ? mx * c2 : m;
-          const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
-          m = mnew;
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < DBH; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-        const float muse = m == -INFINITY ? 0.f : m;   // rows with no key yet: p = 0
-        bf16x8 pB[K16];
-#pragma unroll
-        for (int kb = 0; kb < NB32; ++kb)
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hs + j], c2, -muse));
-              l += p;
-              pB[2 * kb + hs][j] = (__bf16)p;
-            }
-        if constexpr (DBH <= 4 && DS != 2) {
-          // k-step outer: the DBH accumulators are independent, so
-          // consecutive MFMAs do not wait on each other; each V operand is
-          // read one MFMA ahead (scheduling fences hold the order)
-          bf16x8 cur = trans_operand<D>(Vs, 0, dh * DBH * 32, 0, lane);
-#pragma unroll
-          for (int x = 0; x < K16 * DBH; ++x) {
-            const int ks = x / DBH, db = x % DBH;
-            bf16x8 nxt = cur;
-            if (x + 1 < K16 * DBH) {
-              nxt = trans_operand<D>(Vs, 0, (dh * DBH + (x + 1) % DBH) * 32, (x + 1) / DBH, lane);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            acc[db] = mfma32(cur, pB[ks], acc[db]);
-            __builtin_amdgcn_sched_barrier(0);
-            cur = nxt;
-          }
-        } else if constexpr (DBH <= 4) {
-          // k-step outer, operands read where the compiler places them
-#pragma unroll
-          for (int ks = 0; ks < K16; ++ks)
-#pragma unroll
-            for (int db = 0; db < DBH; ++db)
-              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
-        } else {
-#pragma unroll
-          for (int db = 0; db < DBH; ++db) {
-#pragma unroll
-            for (int ks = 0; ks < K16; ++ks)
-              acc[db] = mfma32(trans_operand<D>(Vs, 0, (dh * DBH + db) * 32, ks, lane), pB[ks], acc[db]);
-            if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-    };
-    static_assert(NS >= 2 && NS <= 4, "ring depth");
-    if constexpr (D <= 128) {
-      // unrolled by the ring depth (small head dims: registers to spare)
-      int it = 0;
-      for (; it + NS <= ntiles; it += NS) {
-        step(it, IntC<0>{});
-        step(it + 1, IntC<1>{});
-        if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
-        if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
-      }
-      if (it < ntiles) step(it, IntC<0>{});
-      if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
-      if constexpr (NS == 4)
-        if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
-    } else {
-      for (int it = 0; it < ntiles; ++it) step(it, it % NS);
-    }
-  }
-
-  // Epilogue: combine the two halves' partial sums, normalise, write.
-  const float lt = l + swap_halves(l);
-  const bool has = qvalid && lt > 0.f;
-  const float inv = has ? 1.f / lt : 0.f;
-  if (my_r < b.seglen) {
-    uint16_t* orow = o + qrow * ostride + (int64_t)h * D;
-#pragma unroll
-    for (int db = 0; db < DBH; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
-        union { __bf16 h[4]; uint2 u; } pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = pk.u;
-      }
-    if (hf == 0 && dh == 0)
-      lse[(int64_t)h * pr.Tld + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-  }
-}
-
-// The forward above for head dims a wave holds whole (D <= 128), with
-// cheaper addressing: K tiles in NS slots, then V tiles in NS slots, in a
-// statically sized LDS block, so one base register per row pattern reaches
-// every slot by an immediate offset and every 16-byte chunk by one XOR
-// (lds_tiles.h); tiles are loaded with a scalar tile address plus per-lane
-// offsets fixed for the kernel (rows clamped only on a partial tile).  Same
-// schedule and arithmetic as fwd_mfma_kernel with DS = 1.
-template <int D, int BN, int NW, int NS>
+// K tiles sit in NS slots, then V tiles in NS slots, in a statically sized
+// LDS block, so one base register per row pattern reaches every slot by an
+// immediate offset and every 16-byte chunk by one XOR (lds_tiles.h); tiles
+// are loaded with a scalar tile address plus per-lane offsets fixed for the
+// kernel (rows clamped only on a partial tile).  Head dims up to 256 are
+// held whole by a wave; at 512 a pair of waves splits the head dim (DS = 2,
+// the partial scores meet in an LDS block after the K/V slots).
+template <int D, int BN, int NW, int NS, int DS = 1>
 struct LeanCfg {
   static constexpr int TILE_BYTES = BN * D * 2;     // one K (or V) tile
   static constexpr int V_REGION = NS * TILE_BYTES;  // V slots start here
-  static constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
+  static constexpr int XCH_REGION = 2 * NS * TILE_BYTES;              // partial scores (DS = 2)
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * BN / 2 * 4 : 0;  // BN/2 floats per lane and wave
+  static constexpr int LDS_BYTES = XCH_REGION + XCH_BYTES;
   static constexpr int KBLK = TILE_BYTES / 1024;    // 1 KiB blocks per tile
   // waves that load tiles (the first NWL): the largest power of two <= NW
   // that divides the tile's blocks
@@ -399,18 +68,26 @@ struct LeanCfg {
   static_assert(V_REGION + (NS - 1) * TILE_BYTES <= 65536 + V_REGION, "immediate offsets reach every slot");
 };
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64)
     fwd_lean_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     uint16_t* __restrict__ o, float* __restrict__ lse) {
-  using C = LeanCfg<D, BN, NW, NS>;
-  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
+  using C = LeanCfg<D, BN, NW, NS, DS>;
+  // DS = 2: the waves 2j and 2j+1 (on different SIMDs) share 32 query rows,
+  // each holding half of the head dim (Q^T, the O accumulator and its share
+  // of the scores); the two partial score tiles meet in LDS and both waves
+  // form own + partner, the same bits in both (addition commutes)
+  constexpr int DH = D / DS;
+  constexpr int KT = DH / 16, NB32 = BN / 32, DB = DH / 32, K16 = BN / 16;
+  static_assert(DS == 1 || (DS == 2 && (KT & (KT - 1)) == 0 && (DB & (DB - 1)) == 0), "head-dim halves");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BM = 32 * NW / HG;
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dh = DS > 1 ? (wave_id & (DS - 1)) : 0;      // head-dim half of this wave
+  const int wave = DS > 1 ? wave_id / DS : wave_id;       // row slot of the wave (pair)
+  const int BM = 32 * (NW / DS) / HG;
   const int NB = GB.off[G.n];
   const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;
@@ -447,7 +124,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
   for (int kk = 0; kk < KT; ++kk) {
     uint4 z = {0, 0, 0, 0};
-    if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf);
+    if (qvalid) z = *reinterpret_cast<const uint4*>(q + qrow * ostride + (int64_t)h * D + dh * DH + 16 * kk + 8 * hf);
     qB[kk] = __builtin_bit_cast(bf16x8, z);
   }
   wait_vmcnt<0>();
@@ -468,6 +145,12 @@ __global__ void __launch_bounds__(NW * 64)
   trans_bases<D>(lane, vb0, vb1);                         // V transposed operands
   vb0 += C::V_REGION;
   vb1 += C::V_REGION;
+  if constexpr (DS > 1) {
+    // this wave's half: k-steps dh*KT.. of the K rows, column blocks dh*DB.. of V
+    kbase ^= (unsigned)(dh * KT) << 5;
+    vb0 ^= (unsigned)(dh * DB) << 6;
+    vb1 ^= (unsigned)(dh * DB) << 6;
+  }
 
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
@@ -476,13 +159,13 @@ __global__ void __launch_bounds__(NW * 64)
     const unsigned row_bytes = (unsigned)(rs * 2);
     unsigned voff[C::BPW];
 #pragma unroll
-    for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::BPW + j, lane, row_bytes);
+    for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave_id * C::BPW + j, lane, row_bytes);
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     auto issue = [&](int t) {
-      if (C::NWL < NW && wave >= C::NWL) return;    // not a loading wave
+      if (C::NWL < NW && wave_id >= C::NWL) return;    // not a loading wave
       const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
-      const unsigned kdst = lds0 + (unsigned)((t % NS) * C::TILE_BYTES + wave * C::BPW * 1024);
+      const unsigned kdst = lds0 + (unsigned)((t % NS) * C::TILE_BYTES + wave_id * C::BPW * 1024);
       const unsigned vdst = kdst + C::V_REGION;
       const uint16_t* kg = k + off;
       const uint16_t* vg = v + off;
@@ -499,7 +182,7 @@ __global__ void __launch_bounds__(NW * 64)
         asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
 #pragma unroll
         for (int j = 0; j < C::BPW; ++j) {
-          const int row = (wave * C::BPW + j) * RPB + ln / CPR;
+          const int row = (wave_id * C::BPW + j) * RPB + ln / CPR;
           const int src = min(row, kt.lim - 1);
           const unsigned vo = (unsigned)src * row_bytes + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
           dma_block(kg, vo, kdst + j * 1024);
@@ -551,6 +234,31 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
           for (int kb = 0; kb < NB32; ++kb) ka[kb] = kn[kb];
         }
+      }
+      if constexpr (DS > 1) {
+        // partial scores of this half out, the partner's in (every wave, also
+        // on a skipped tile, so that the barrier is reached by all)
+        float4* xch = reinterpret_cast<float4*>(reinterpret_cast<char*>(lds) + C::XCH_REGION);
+        float4* xw = xch + wave_id * 64 * (4 * NB32);
+        const float4* xp = xch + (wave_id ^ 1) * 64 * (4 * NB32);
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xw[(4 * kb + j) * 64 + lane] = make_float4(s[kb][4 * j], s[kb][4 * j + 1], s[kb][4 * j + 2], s[kb][4 * j + 3]);
+        block_sync();
+#pragma unroll
+        for (int kb = 0; kb < NB32; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 t = xp[(4 * kb + j) * 64 + lane];
+            s[kb][4 * j] += t.x;
+            s[kb][4 * j + 1] += t.y;
+            s[kb][4 * j + 2] += t.z;
+            s[kb][4 * j + 3] += t.w;
+          }
+      }
+      if (kind != 0) {
         if (kind == 2) {
           int d0 = qpos - kt.pos0 - 4 * hf;
           int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
@@ -610,15 +318,16 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     };
-    static_assert(NS == 3, "ring of three, unrolled by three");
+    static_assert(NS == 2 || NS == 3, "ring of two or three, unrolled by its depth");
     int it = 0;
     for (; it + NS <= ntiles; it += NS) {
       step(it, IntC<0>{});
       step(it + 1, IntC<1>{});
-      step(it + 2, IntC<2>{});
+      if constexpr (NS == 3) step(it + 2, IntC<2 % NS>{});
     }
     if (it < ntiles) step(it, IntC<0>{});
-    if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+    if constexpr (NS == 3)
+      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
   }
 
   const float lt = l + swap_halves(l);
@@ -630,13 +339,13 @@ __global__ void __launch_bounds__(NW * 64)
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hf;
+        const int d = dh * DH + db * 32 + 8 * g4 + 4 * hf;
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * inv);
         *reinterpret_cast<uint2*>(orow + d) = pk.u;
       }
-    if (hf == 0)
+    if (hf == 0 && dh == 0)
       lse[(int64_t)h * pr.Tld + qrow] = has ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
@@ -652,14 +361,14 @@ struct FwdPlan {
 
 FwdPlan plan(const Problem& pr, const Groups& G) {
   FwdPlan p;
-  // Per wave, Q^T and the O accumulator take 3*D/4 registers: two waves per
-  // SIMD fit up to D = 128; D = 256 splits the head dim over wave pairs and
-  // D = 512 over groups of four waves, so every head dim runs eight waves,
-  // two per SIMD (at D = 512 four-way instead of two-way with one wave per
-  // SIMD: 12% less forward time on the Gemma-style global layer).
+  // Per wave, Q^T and the O accumulator take 3*D/4 registers.  With the
+  // XOR-derived operand addresses a wave holds D = 256 whole at two waves
+  // per SIMD (242 registers; 32-key tiles) and D = 128 at three (twelve
+  // waves, 164 registers); D = 512 splits the head dim over wave pairs
+  // (247 registers, two waves per SIMD).
   p.NW = pr.D == 128 ? 12 : 8;
   p.BN = pr.D <= 128 ? 64 : 32;
-  p.DS = pr.D <= 256 ? 1 : 4;
+  p.DS = pr.D <= 256 ? 1 : 2;
   p.HG = 1;   // query heads per block: a power of two dividing g and the waves' row slots
   while (p.HG * 2 <= p.NW / p.DS && pr.g % (p.HG * 2) == 0 && (p.NW / p.DS) % (p.HG * 2) == 0) p.HG *= 2;
   p.BM = 32 * (p.NW / p.DS) / p.HG;
@@ -680,26 +389,13 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
   return p;
 }
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS = 1>
 hipError_t run_lean(const Problem& pr, const Groups& G, const FwdPlan& p, const void* q, const void* k,
                     const void* v, void* o, float* lse, hipStream_t stream) {
-  static_assert(LeanCfg<D, BN, NW, NS>::LDS_BYTES <= 160 * 1024, "LDS budget");
-  return launch("fwd", fwd_lean_kernel<D, BN, NW, NS>, dim3((unsigned)p.nwg), dim3(NW * 64), 0, stream, pr, G,
+  static_assert(LeanCfg<D, BN, NW, NS, DS>::LDS_BYTES <= 160 * 1024, "LDS budget");
+  return launch("fwd", fwd_lean_kernel<D, BN, NW, NS, DS>, dim3((unsigned)p.nwg), dim3(NW * 64), 0, stream, pr, G,
                 p.gb, p.HG, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                 static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse);
-}
-
-template <int D, int BN, int NW, int NS, int DS>
-hipError_t run(const Problem& pr, const Groups& G, const FwdPlan& p, const void* q, const void* k, const void* v,
-               void* o, float* lse, hipStream_t stream) {
-  using C = FwdCfg<D, BN, NW, NS, DS>;
-  static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = allow_lds(fwd_mfma_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
-  return launch("fwd", fwd_mfma_kernel<D, BN, NW, NS, DS>, dim3((unsigned)p.nwg), dim3(NW * 64), C::LDS_BYTES,
-                stream, pr, G, p.gb, p.HG, static_cast<const uint16_t*>(q),
-                static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                static_cast<uint16_t*>(o), lse);
 }
 
 }  // namespace
@@ -718,7 +414,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
     case 64: return run_lean<64, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 128: return run_lean<128, 64, 12, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 256: return run_lean<256, 32, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
-    case 512: return run<512, 32, 8, 2, 4>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
+    case 512: return run_lean<512, 32, 8, 2, 2>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
 }
