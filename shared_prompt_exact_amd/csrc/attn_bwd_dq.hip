@@ -391,9 +391,5 @@ template hipError_t launch_bwd_dq<128, 32, 8, 3, 1>(const Problem&, const Groups
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);
-template hipError_t launch_bwd_dq<512, 32, 8, 2, 4>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
-                                                    const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
-                                                    uint16_t*, hipStream_t);
 
 }  // namespace dualkv

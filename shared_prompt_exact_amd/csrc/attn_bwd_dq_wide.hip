@@ -1,20 +1,22 @@
-// dQ kernel of the shared-prompt attention backward at head dim 256 on
-// gfx950 matrix cores, one wave per SIMD, without splitting the head dim.
+// dQ kernel of the shared-prompt attention backward at head dims 256 and 512
+// on gfx950 matrix cores, one wave per SIMD: a wave holds the whole head dim
+// at 256, and half of it at 512 (a wave pair shares the rows and exchanges
+// partial S and dP tiles through LDS).
 //
 // "DualKV: Shared-Prompt Flash Attention ..." (arXiv 2605.15422), Abstract:
 // the backward iterates over the same two disjoint key regions as the
 // forward.  Per visible (query i, key j) pair: p = exp(scale q.k - LSE_i),
 // dp = dO_i . v_j, ds = p (dp - Delta_i), dQ_i += scale ds k_j.  The tiling
 // is that of bwd_dq_kernel (query-parallel, S and dP recomputed, dQ
-// accumulated in registers and written once), with Q^T and dO^T in 128
-// VGPRs and the 32 x 256 dQ accumulator in accumulation registers: this
+// accumulated in registers and written once), with Q^T and dO^T (256 dims)
+// in 128 VGPRs and the 32 x 256 dQ accumulator in accumulation registers: this
 // file is compiled without forcing MFMA results into VGPRs, which is what
 // lets one wave hold all of it.  K and V tiles: NS slots each in a static
 // LDS block, operand addresses from per-lane bases with one XOR per 16-byte
 // chunk and immediate slot offsets, tile loads from a scalar tile address
-// plus per-lane offsets (lds_tiles.h).  Delta = dO . O of the wave's rows
-// is formed in the prologue and written with LSE * log2(e) for the dK/dV
-// kernel.
+// plus per-lane offsets (lds_tiles.h).  At head dim 256, Delta = dO . O of
+// the wave's rows is formed in the prologue and written with LSE * log2(e)
+// for the dK/dV kernel; at 512 both come from their own kernel.
 #include "lds_tiles.h"
 
 namespace dualkv {
@@ -27,33 +29,40 @@ struct IntC {
   static constexpr int value = V;
 };
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS>
 struct DqWideCfg {
   static constexpr int TILE_BYTES = BN * D * 2;     // one K (or V) tile
   static constexpr int V_REGION = NS * TILE_BYTES;  // V slots start here
-  static constexpr int LDS_BYTES = 2 * NS * TILE_BYTES;
+  static constexpr int XCH_REGION = 2 * NS * TILE_BYTES;              // partial S, dP (DS = 2)
+  static constexpr int XCH_BYTES = DS > 1 ? NW * 64 * BN * 4 : 0;     // 2 x BN/2 floats per lane
+  static constexpr int LDS_BYTES = XCH_REGION + XCH_BYTES;
   static constexpr int KBLK = TILE_BYTES / 1024;    // 1 KiB blocks per tile
   static constexpr int BPW = KBLK / NW;             // blocks per wave per tile (K and V each)
   static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
-  static_assert(V_REGION <= 65536, "immediate offsets reach every slot");
+  static_assert((NS - 1) * TILE_BYTES + 16 * 2 * D < 65536, "immediate offsets reach every slot");
 };
 
-template <int D, int BN, int NW, int NS>
+template <int D, int BN, int NW, int NS, int DS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     bwd_dq_wide_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                        const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                        const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
                        const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ lse2w,
                        uint16_t* __restrict__ dq) {
-  using C = DqWideCfg<D, BN, NW, NS>;
-  constexpr int DS = 1;
-  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, KTH = KT, NWQ = NW;
+  using C = DqWideCfg<D, BN, NW, NS, DS>;
+  // DS = 2: waves 2j and 2j+1 share 32 query rows, each holding half of the
+  // head dim (Q^T, dO^T and the dQ accumulator); their partial S and dP
+  // tiles meet in LDS and both form own + partner (the same bits in both)
+  constexpr int DH = D / DS;
+  constexpr int KTH = DH / 16, NB32 = BN / 32, DB = DH / 32, NWQ = NW / DS;
   static_assert(NB32 == 1, "32-key tiles");
+  static_assert(DS == 1 || (DS == 2 && (KTH & (KTH - 1)) == 0 && (DB & (DB - 1)) == 0), "head-dim halves");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave;
+  const int dh = DS > 1 ? (wave & (DS - 1)) : 0;       // head-dim half of this wave
+  const int wq = DS > 1 ? wave / DS : wave;            // row slot
   const int BM = 32 * NWQ / HG;
   const int NB = GB.off[G.n];                 // row blocks of all groups, per head group
   const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
@@ -96,7 +105,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
   for (int kk = 0; kk < KTH; ++kk) {
     uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (qvalid) {
-      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf;
+      const int64_t off = qrow * ostride + (int64_t)h * D + dh * DH + 16 * kk + 8 * hf;
       z = *reinterpret_cast<const uint4*>(q + off);
       y = *reinterpret_cast<const uint4*>(dout + off);
     }
@@ -151,6 +160,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
   unsigned kbase = row_base<D>(l32, hf);
   unsigned tb0, tb1;
   trans_bases<D>(lane, tb0, tb1);
+  if constexpr (DS > 1) {
+    // this wave's half: k-steps dh*KTH.. of the K and V rows, column blocks
+    // dh*DB.. of K^T
+    kbase ^= (unsigned)(dh * KTH) << 5;
+    tb0 ^= (unsigned)(dh * DB) << 6;
+    tb1 ^= (unsigned)(dh * DB) << 6;
+  }
+  unsigned vbase = kbase + C::V_REGION;        // V rows: the K bases in the V slots
 
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
@@ -183,29 +200,29 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
       if (t < ntiles) issue(t);
     auto step = [&](int it, auto slot_c) {
       constexpr int SLOT = decltype(slot_c)::value;
-      constexpr unsigned KIMM = SLOT * C::TILE_BYTES, VIMM = C::V_REGION + SLOT * C::TILE_BYTES;
+      constexpr unsigned KIMM = SLOT * C::TILE_BYTES, VIMM = SLOT * C::TILE_BYTES;
       if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
       else wait_vmcnt<0>();
       block_sync();
       if (it + NS - 1 < ntiles) issue(it + NS - 1);
-      asm volatile("" : "+v"(kbase), "+v"(tb0), "+v"(tb1));   // XORs recomputed per tile
+      asm volatile("" : "+v"(kbase), "+v"(vbase), "+v"(tb0), "+v"(tb1));   // XORs recomputed per tile
       const KeyTile kt = tile_at(pr, b, tr, it, BN);
       const int kind = tile_kind(pr, kt, BN, w_any, w_all, wq_lo, wq_hi);
-      if (kind == 0) return;
+      if (DS == 1 && kind == 0) return;
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      {
+      if (kind != 0) {
         // S^T = K Q^T and dP^T = V dO^T; the operands of k-step kk+2 are read
         // before the MFMAs of step kk (scheduling fences keep them there)
-        bf16x8 k0 = row_operand_x<D>(lds, kbase, 0, KIMM), v0 = row_operand_x<D>(lds, kbase, 0, VIMM);
-        bf16x8 k1 = row_operand_x<D>(lds, kbase, 1, KIMM), v1 = row_operand_x<D>(lds, kbase, 1, VIMM);
+        bf16x8 k0 = row_operand_x<D>(lds, kbase, 0, KIMM), v0 = row_operand_x<D>(lds, vbase, 0, VIMM);
+        bf16x8 k1 = row_operand_x<D>(lds, kbase, 1, KIMM), v1 = row_operand_x<D>(lds, vbase, 1, VIMM);
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
+        for (int kk = 0; kk < KTH; ++kk) {
           bf16x8 k2 = k1, v2 = v1;
-          if (kk + 2 < KT) {
+          if (kk + 2 < KTH) {
             k2 = row_operand_x<D>(lds, kbase, kk + 2, KIMM);
-            v2 = row_operand_x<D>(lds, kbase, kk + 2, VIMM);
+            v2 = row_operand_x<D>(lds, vbase, kk + 2, VIMM);
             __builtin_amdgcn_sched_barrier(0);
           }
           s = mfma32(k0, qB[kk], s);
@@ -213,6 +230,26 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
           __builtin_amdgcn_sched_barrier(0);
           k0 = k1; k1 = k2;
           v0 = v1; v1 = v2;
+        }
+      }
+      if constexpr (DS > 1) {
+        // partial S and dP of this half out, the partner's in (every wave,
+        // also on a skipped tile, so that the barrier is reached by all)
+        float4* xch = reinterpret_cast<float4*>(reinterpret_cast<char*>(lds) + C::XCH_REGION);
+        float4* xw = xch + wave * 64 * 8;
+        const float4* xp = xch + (wave ^ 1) * 64 * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xw[j * 64 + lane] = make_float4(s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]);
+          xw[(4 + j) * 64 + lane] = make_float4(dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]);
+        }
+        block_sync();
+        if (kind == 0) return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = xp[j * 64 + lane], u = xp[(4 + j) * 64 + lane];
+          s[4 * j] += t.x; s[4 * j + 1] += t.y; s[4 * j + 2] += t.z; s[4 * j + 3] += t.w;
+          dp[4 * j] += u.x; dp[4 * j + 1] += u.y; dp[4 * j + 2] += u.z; dp[4 * j + 3] += u.w;
         }
       }
       if (kind == 2) {
@@ -255,15 +292,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
         c1 = c2n;
       }
     };
-    static_assert(NS == 3, "ring of three, unrolled by three");
+    static_assert(NS == 2 || NS == 3, "ring of two or three, unrolled by its depth");
     int it = 0;
     for (; it + NS <= ntiles; it += NS) {
       step(it, IntC<0>{});
       step(it + 1, IntC<1>{});
-      step(it + 2, IntC<2>{});
+      if constexpr (NS == 3) step(it + 2, IntC<2 % NS>{});
     }
     if (it < ntiles) step(it, IntC<0>{});
-    if (it + 1 < ntiles) step(it + 1, IntC<1>{});
+    if constexpr (NS == 3)
+      if (it + 1 < ntiles) step(it + 1, IntC<1>{});
   }
 
   if (my_r < b.seglen) {
@@ -275,7 +313,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g4 + 4 * hf) = pk.u;
+        *reinterpret_cast<uint2*>(orow + dh * DH + db * 32 + 8 * g4 + 4 * hf) = pk.u;
       }
   }
 }
@@ -286,10 +324,18 @@ hipError_t launch_bwd_dq_wide(const Problem& pr, const Groups& G, const GroupBlo
                               const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                               const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
                               hipStream_t stream) {
-  constexpr int D = 256, BN = 32, NW = 4, NS = 3;
-  static_assert(DqWideCfg<D, BN, NW, NS>::LDS_BYTES <= 160 * 1024, "LDS budget");
-  return launch("bwd_dq", bwd_dq_wide_kernel<D, BN, NW, NS>, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, pr, G,
-                gb, HG, q, k, v, dout, o, lse, delta, lse2, dq);
+  constexpr int BN = 32, NW = 4;
+  if (pr.D == 256) {
+    static_assert(DqWideCfg<256, BN, NW, 3, 1>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dq", bwd_dq_wide_kernel<256, BN, NW, 3, 1>, dim3((unsigned)nwg), dim3(NW * 64), 0, stream,
+                  pr, G, gb, HG, q, k, v, dout, o, lse, delta, lse2, dq);
+  }
+  if (pr.D == 512) {
+    static_assert(DqWideCfg<512, BN, NW, 2, 2>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dq", bwd_dq_wide_kernel<512, BN, NW, 2, 2>, dim3((unsigned)nwg), dim3(NW * 64), 0, stream,
+                  pr, G, gb, HG, q, k, v, dout, o, lse, delta, lse2, dq);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dualkv

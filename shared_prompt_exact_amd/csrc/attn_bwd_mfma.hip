@@ -959,14 +959,14 @@ __global__ void __launch_bounds__(256)
 // most 256 dims of its operands and accumulators (VGPRs plus accumulation
 // registers), and the waves of a workgroup cover several 32-row (or
 // 32-key) slices that share each streamed tile.
-inline int dq_waves(int D) { return D == 256 ? 4 : 8; }
+inline int dq_waves(int D) { return D >= 256 ? 4 : 8; }
 inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
 // Key tiles per wave of the dK/dV kernel.  Two tiles (one wave per SIMD)
 // halve the LDS reads per MFMA but lose the second wave's latency hiding;
 // measured slower at D = 128 (11.6 ms against 9.9 ms on the Qwen3-8B-shaped
 // layer), so every head dim runs one tile per wave.
 inline int kv_tiles_per_wave(int) { return 1; }
-inline int dq_split(int D) { return D <= 256 ? 1 : 4; }
+inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
 inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
 struct BwdPlan {
@@ -1132,7 +1132,7 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_dq > 0) {
-    if constexpr (D == 256 && DS == 1 && NW == 4)
+    if constexpr ((D == 256 && DS == 1 && NW == 4) || (D == 512 && DS == 2 && NW == 4))
       e = launch_bwd_dq_wide(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16, static_cast<const uint16_t*>(o),
                              lse, delta, lse2, static_cast<uint16_t*>(dq), stream);
     else
@@ -1180,7 +1180,7 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
     case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 8, 4, 32, 2, 2, 4, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
