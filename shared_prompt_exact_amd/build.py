@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdualkv.so")
 SOURCES = ["repack.hip", "attn_scalar.hip", "attn_fwd_mfma.hip", "attn_bwd_mfma.hip", "attn_bwd_dq.hip",
-           "attn_bwd_dq_wide.hip", "api.hip", "profile.hip", "gemm.hip", "layer_ops.hip", "layer.hip"]
+           "attn_bwd_dq_wide.hip", "attn_bwd_dkdv_wide.hip", "api.hip", "profile.hip", "gemm.hip", "layer_ops.hip", "layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -30,7 +30,7 @@ FLAGS = [
 # Not for the one-wave-per-SIMD kernels whose accumulators live in the
 # accumulation registers.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-AGPR_ACCUMULATORS = {"attn_bwd_dq_wide.hip"}
+AGPR_ACCUMULATORS = {"attn_bwd_dq_wide.hip", "attn_bwd_dkdv_wide.hip"}
 
 
 def _compile(src: str) -> tuple[str, int, str]:

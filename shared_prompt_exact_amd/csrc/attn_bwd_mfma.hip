@@ -27,6 +27,7 @@
 // order, so results are bitwise reproducible.
 #include <algorithm>
 
+#include "kv_items.h"
 #include "lds_tiles.h"
 
 namespace dualkv {
@@ -35,8 +36,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // --------------------------------------------------------------- dkdv kernel
-
-constexpr int kStageRows = 32;
 
 template <int D, int NWK, int NS, int DS, bool VREG, int KW>
 struct KvCfg {
@@ -57,87 +56,6 @@ struct KvCfg {
   static constexpr int SBPW = 2 * QBLK / NWK;               // stage blocks per wave
   static_assert(V_ELEMS * 2 % (1024 * NWK) == 0 && 2 * QBLK % NWK == 0, "even split");
 };
-
-// Work item of the dK/dV kernel.
-struct KvItem {
-  int c;          // KV head
-  int seg;        // -1: prompt key tile; else response n
-  int k0;         // first key row inside its segment
-  int slot;       // prompt tiles: slot (0 = prompt queries, s >= 1 = responses)
-};
-
-// Walks (segment, 32-row stage, query head) in a fixed order.
-struct StageIter {
-  int seg, seg_last;
-  int r, r_end;       // current stage row and the segment's row bound
-  int h, h0, h1;
-  int svalid;         // valid rows of the current segment (read once per segment)
-  bool ok;
-};
-
-struct KvShape {
-  int slots;          // slots per prompt tile
-  int per_slot;       // responses per slot (slots >= 2)
-  int nPt, nRt;       // prompt / response key tiles per KV head
-  int t0;             // first prompt tile a response query can see (window)
-};
-
-// Work items of the dK/dV kernel per prompt group: group i owns items
-// [off[i], off[i+1]) of every KV head, has key tiling sh[i] and writes its
-// prompt partials from float part[i] of the partial buffers.
-struct KvGroups {
-  int off[kMaxGroups + 1];
-  KvShape sh[kMaxGroups];
-  int64_t part[kMaxGroups];
-  LaunchOrder ord;    // places the groups' items in the launch
-};
-static_assert(sizeof(Problem) + sizeof(Groups) + sizeof(KvGroups) + 16 * sizeof(void*) <= 4096,
-              "dK/dV kernel arguments");
-
-// Rows [lo, hi) of segment `seg` that can see keys [kp_lo, kp_hi] (logical
-// positions) of the item; lo is rounded down to a stage boundary.
-__device__ __forceinline__ void seg_rows(const Problem& pr, int seg, int kp_lo, int kp_hi, int& lo,
-                                         int& hi, int& Lv) {
-  if (seg < 0) {
-    lo = (kp_lo / kStageRows) * kStageRows;
-    hi = pr.W > 0 ? min(pr.P, kp_hi + pr.W) : pr.P;
-    Lv = pr.P;
-  } else {
-    Lv = resp_valid(pr, seg);
-    const int rlo = max(0, kp_lo - pr.P);
-    lo = (rlo / kStageRows) * kStageRows;
-    hi = Lv;
-    if (pr.W > 0) hi = min(hi, max(0, kp_hi + pr.W - pr.P));
-  }
-}
-
-__device__ __forceinline__ void iter_fix(const Problem& pr, StageIter& s, int kp_lo, int kp_hi) {
-  // move to the first non-empty segment at or after s.seg
-  while (s.seg <= s.seg_last) {
-    int lo, hi, Lv;
-    seg_rows(pr, s.seg, kp_lo, kp_hi, lo, hi, Lv);
-    if (s.r < lo) s.r = lo;
-    if (s.r < hi) {
-      s.r_end = hi;
-      s.svalid = Lv;
-      s.ok = true;
-      return;
-    }
-    ++s.seg;
-    s.r = 0;
-  }
-  s.ok = false;
-}
-
-__device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int kp_lo, int kp_hi) {
-  if (++s.h < s.h1) return;
-  s.h = s.h0;
-  s.r += kStageRows;
-  if (s.r < s.r_end) return;
-  ++s.seg;
-  s.r = 0;
-  iter_fix(pr, s, kp_lo, kp_hi);
-}
 
 // DS = 2: a wave pair owns the same 32 keys, each half of the head dim (K^T
 // and V^T operands, the S / dP contractions and the dK / dV accumulators);
@@ -565,6 +483,8 @@ __global__ void __launch_bounds__(NWK * 64)
   constexpr unsigned V_BYTES = C::V_ELEMS * 2, Q_BYTES = C::Q_ELEMS * 2, DO_BYTES = C::DO_ELEMS * 2;
   constexpr unsigned STAGE_BYTES = C::STAGE * 2;
   static_assert(C::SBPW == 2 && C::QBLK == NWK, "one Q block and one dO block per wave and stage");
+  static_assert(V_BYTES % (2 * D) == 0 && STAGE_BYTES % (2 * D) == 0,
+                "slot offsets added to operand bases leave the XOR-addressed bits alone");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1109,7 +1029,9 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
                char* ws, hipStream_t stream) {
   using CK = KvCfg<D, NWK, KVNS, KDS, VREG, KW>;
   static_assert(CK::LDS_BYTES <= 160 * 1024, "LDS budget");
-  if constexpr (!(D == 128 && KDS == 1 && !VREG && KW == 1)) {
+  constexpr bool kv_lean = D == 128 && KDS == 1 && !VREG && KW == 1;
+  constexpr bool kv_wide = D == 256 && KDS == 1 && VREG && KW == 1 && NWK == 4;
+  if constexpr (!kv_lean && !kv_wide) {
     static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
     if (a2 != hipSuccess) return a2;
   }
@@ -1142,10 +1064,13 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
-    if constexpr (D == 128 && KDS == 1 && !VREG && KW == 1)
+    if constexpr (kv_lean)
       e = launch("bwd_dkdv", bwd_dkdv_lean_kernel<D, NWK, KVNS>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), 0,
                  stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                  static_cast<uint16_t*>(dv), pk, pv);
+    else if constexpr (kv_wide)
+      e = launch_bwd_dkdv_wide(pr, G, p.kg, p.nwg_kv, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
+                               static_cast<uint16_t*>(dv), pk, pv, stream);
     else
       e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64),
                  CK::LDS_BYTES, stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
