@@ -29,16 +29,20 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The compiler does not see into inline assembly, so these MFMAs carry
+// their own waits: two wait states before each (a vector instruction that
+// wrote an operand register just before), and the settle below after the
+// last of a chain.
 // C = A B into VGPRs (first k-step: no accumulator input).
 __device__ __forceinline__ f32x16 mfma_v_first(bf16x8 a, bf16x8 b) {
   f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 // C += A B, C in VGPRs (the accumulator is the result of the previous MFMA
 // of the same chain: back-to-back accumulation needs no wait).
 __device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 // One accumulator element moved to a VGPR where it is used: the asm takes
 // its operand in the accumulation register file, so the compiler keeps the
