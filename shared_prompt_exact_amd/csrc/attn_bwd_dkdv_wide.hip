@@ -1,6 +1,6 @@
-// dK/dV kernel of the shared-prompt attention backward at head dim 256 on
-// gfx950 matrix cores, one wave per SIMD, accumulators in the accumulation
-// registers.
+// dK/dV kernel of the shared-prompt attention backward at head dims 256 and
+// 512 on gfx950 matrix cores, one wave per SIMD, accumulators in the
+// accumulation registers (at 512 a wave pair splits the head dim).
 //
 // "DualKV: Shared-Prompt Flash Attention ..." (arXiv 2605.15422), Abstract:
 // the gradient of a shared-prompt key or value sums the contributions of
@@ -10,10 +10,13 @@
 // LSE_i), dp = dO_i . v_j, ds = p (dp - Delta_i), dV_j += p dO_i,
 // dK_j += scale ds q_i.
 //
-// Registers of a wave (32 keys): K^T of its keys (64 VGPRs), the 32 x 256
-// fp32 dK and dV accumulators (256 accumulation registers), and the S and
-// dP tiles of the current stage; the item's V tile stays in LDS (row
-// operands of dP) beside a ring of two Q / dO stages.  This file is built without
+// Registers of a wave (32 keys, 256 head dims: all of them at head dim 256,
+// one half at 512): K^T of its keys (64 VGPRs), the 32 x 256 fp32 dK and dV
+// accumulators (256 accumulation registers), and the S and dP tiles of the
+// current stage.  At head dim 256 the item's V tile stays in LDS (row
+// operands of dP) beside a ring of two Q / dO stages; at 512 V^T of the
+// wave's half is in registers too, and the pair's partial S and dP tiles
+// meet in LDS.  This file is built without
 // forcing MFMA results into VGPRs, so the accumulators live in the
 // accumulation registers; S and dP, for which no accumulation register is
 // left, are formed by MFMAs written as inline assembly with VGPR results
@@ -61,10 +64,11 @@ __device__ __forceinline__ void mfma_v_settle(f32x16& s, f32x16& dp) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s), "+v"(dp));
 }
 
-template <int D, int NWK, int NS>
+template <int D, int NWK, int NS, int KDS>
 struct KvWideCfg {
-  static constexpr int BK = 32 * NWK;                    // keys per workgroup
-  static constexpr int V_BYTES = BK * D * 2;             // the item's V tile, loaded once
+  static constexpr int BK = 32 * NWK / KDS;              // keys per workgroup
+  // KDS = 1: the item's V tile in LDS, loaded once; KDS = 2: V^T in registers
+  static constexpr int V_BYTES = KDS == 1 ? BK * D * 2 : 0;
   static constexpr int VBPW = V_BYTES / 1024 / NWK;      // its 1 KiB blocks per wave
   static constexpr int Q_BYTES = kStageRows * D * 2;     // one stage's Q rows (and dO rows)
   static constexpr int STAT_BYTES = 2 * kStageRows * 4;  // lse2 and delta of the stage's rows
@@ -72,7 +76,10 @@ struct KvWideCfg {
   // added to an operand base then leaves the bits that the per-chunk XORs
   // address untouched
   static constexpr int STAGE_BYTES = (2 * Q_BYTES + STAT_BYTES + 2 * D - 1) / (2 * D) * (2 * D);
-  static constexpr int LDS_BYTES = V_BYTES + NS * STAGE_BYTES;
+  // KDS = 2: partial S (then dP) of every wave, 16 floats per lane
+  static constexpr int XCH_REGION = V_BYTES + NS * STAGE_BYTES;
+  static constexpr int XCH_BYTES = KDS > 1 ? NWK * 64 * 16 * 4 : 0;
+  static constexpr int LDS_BYTES = XCH_REGION + XCH_BYTES;
   static constexpr int QBLK = Q_BYTES / 1024;            // 1 KiB blocks of a Q (or dO) stage
   static constexpr int QPW = QBLK / NWK;                 // Q (and dO) blocks per wave per stage
   static_assert(QBLK % NWK == 0, "stage blocks split evenly over the waves");
@@ -80,7 +87,7 @@ struct KvWideCfg {
   static_assert(Q_BYTES + 16 * 2 * D < 65536, "immediate offsets within a stage (the slot is in the base)");
 };
 
-template <int D, int NWK, int NS>
+template <int D, int NWK, int NS, int KDS>
 __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     bwd_dkdv_wide_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
                          const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -88,11 +95,18 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
                          const float* __restrict__ delta, uint16_t* __restrict__ dk,
                          uint16_t* __restrict__ dv, float* __restrict__ part_k,
                          float* __restrict__ part_v) {
-  using C = KvWideCfg<D, NWK, NS>;
-  constexpr int KT = D / 16, DB = D / 32, BK = C::BK;
+  using C = KvWideCfg<D, NWK, NS, KDS>;
+  // KDS = 2: waves 2j and 2j+1 share 32 keys, each holding half of the head
+  // dim (K^T, V^T, the dK / dV accumulators); their partial S and dP tiles
+  // meet in LDS and both form own + partner (the same bits in both)
+  constexpr int DH = D / KDS;
+  constexpr int KT = DH / 16, DB = DH / 32, BK = C::BK;
+  static_assert(KDS == 1 || (KDS == 2 && KT == 16 && DB == 8), "head-dim halves of 256");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dh = KDS > 1 ? (wave_id & 1) : 0;            // head-dim half of this wave
+  const int wave = KDS > 1 ? wave_id >> 1 : wave_id;     // 32-key slot of the wave (pair)
 
   // ---- decode the work item (the launch order places the groups' items)
   const int per_head = KG.off[G.n];
@@ -144,26 +158,32 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int kp_lo = posoff + it.k0;
   const int kp_hi = posoff + it.k0 + min(BK, max(klim, 1)) - 1;
 
-  // ---- this wave's 32 keys: K^T as B operands in registers; the V tile
-  // row-major in LDS (B operand of dP)
+  // ---- this wave's 32 keys: K^T as B operands in registers; V^T too
+  // (KDS = 2) or the V tile row-major in LDS (KDS = 1, B operand of dP)
   const int wk0 = 32 * wave;
   const int my_k = wk0 + l32;
   const bool kvalid = my_k < klim;
   const int kpos = kp_lo + my_k;
   const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
   const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KT];
+  bf16x8 kB[KT], vB[KDS > 1 ? KT : 1];
 #pragma unroll
   for (int kk = 0; kk < KT; ++kk) {
-    uint4 z = {0, 0, 0, 0};
-    if (kvalid) z = *reinterpret_cast<const uint4*>(k + krow * kstride + (int64_t)c * D + 16 * kk + 8 * hf);
+    uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    const int64_t off = krow * kstride + (int64_t)c * D + dh * DH + 16 * kk + 8 * hf;
+    if (kvalid) {
+      z = *reinterpret_cast<const uint4*>(k + off);
+      if constexpr (KDS > 1) y = *reinterpret_cast<const uint4*>(v + off);
+    }
     kB[kk] = __builtin_bit_cast(bf16x8, z);
+    if constexpr (KDS > 1) vB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   wait_vmcnt<0>();                    // the loop's waits count only LDS loads
   asm volatile("" ::: "memory");
-  if (klim > 0)
-    dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride, min(BK, klim), lds,
-                wave * C::VBPW, C::VBPW, lane);
+  if constexpr (KDS == 1)
+    if (klim > 0)
+      dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride, min(BK, klim), lds,
+                  wave * C::VBPW, C::VBPW, lane);
   const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
@@ -195,28 +215,30 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
-  const bool stat_wave = wave == NWK - 1;    // also loads the stage's lse2 / delta
+  const bool stat_wave = wave_id == NWK - 1;    // also loads the stage's lse2 / delta
 
   // operand bases (bytes from the start of LDS): Q / dO rows l32 of stage 0;
   // Q^T / dO^T transposed reads of stage 0; the stage's statistics for this
   // lane's rows
-  const unsigned vbase = row_base<D>(wk0 + l32, hf);       // V rows of this wave's keys
-  const unsigned qbase = C::V_BYTES + row_base<D>(l32, hf);
+  const unsigned vbase = row_base<D>(wk0 + l32, hf);       // V rows of this wave's keys (KDS = 1)
+  // Q / dO rows: k-steps dh*KT.. of this wave's half; Q^T / dO^T: column
+  // blocks dh*DB.. (the half's bits lie above those the chunk XORs address)
+  const unsigned qbase = C::V_BYTES + (row_base<D>(l32, hf) ^ ((unsigned)(dh * KT) << 5));
   unsigned tb0, tb1;
   trans_bases<D>(lane, tb0, tb1);
-  tb0 += C::V_BYTES;
-  tb1 += C::V_BYTES;
+  tb0 = C::V_BYTES + (tb0 ^ ((unsigned)(dh * DB) << 6));
+  tb1 = C::V_BYTES + (tb1 ^ ((unsigned)(dh * DB) << 6));
   const unsigned sbase = C::V_BYTES + 2u * C::Q_BYTES + (unsigned)(4 * hf) * 4u;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   unsigned voff[C::QPW];
 #pragma unroll
-  for (int j = 0; j < C::QPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::QPW + j, lane, (unsigned)(qstride * 2));
+  for (int j = 0; j < C::QPW; ++j) voff[j] = dma_lane_offset<D>(wave_id * C::QPW + j, lane, (unsigned)(qstride * 2));
 
   auto issue = [&](const StageIter& st, int slot) {
     const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
     const int n = min(kStageRows, st.svalid - st.r);
     const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
-    const unsigned dst = lds0 + C::V_BYTES + (unsigned)slot * C::STAGE_BYTES + (unsigned)(wave * C::QPW) * 1024u;
+    const unsigned dst = lds0 + C::V_BYTES + (unsigned)slot * C::STAGE_BYTES + (unsigned)(wave_id * C::QPW) * 1024u;
     // Q blocks wave*QPW .. and the same dO blocks of the stage
     if (n >= kStageRows) {
 #pragma unroll
@@ -230,7 +252,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
 #pragma unroll
       for (int j = 0; j < C::QPW; ++j) {
-        const int row = (wave * C::QPW + j) * RPB + ln / CPR;
+        const int row = (wave_id * C::QPW + j) * RPB + ln / CPR;
         const int src = min(row, n - 1);   // rows past the last valid one re-read it (finite, masked)
         const unsigned vo = (unsigned)src * (unsigned)(qstride * 2) + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
         dma_block(q + off, vo, dst + j * 1024u);
@@ -274,38 +296,63 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       bf16x8 pB[2], dsB[2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pB[0][j] = pB[1][j] = dsB[0][j] = dsB[1][j] = (__bf16)0.f;
-      if (kind != 0) {
-        // S = Q K^T and dP = dO V^T into VGPRs; the Q and dO operands of
-        // k-step kk+2 are read before the MFMAs of step kk
-        f32x16 s, dp;
-        {
-          bf16x8 q0 = row_operand_x<D>(lds, qb, 0, 0), d0 = row_operand_x<D>(lds, qb, 0, C::Q_BYTES);
-          bf16x8 v0 = row_operand_x<D>(lds, vb, 0, 0);
-          bf16x8 q1 = row_operand_x<D>(lds, qb, 1, 0), d1 = row_operand_x<D>(lds, qb, 1, C::Q_BYTES);
-          bf16x8 v1 = row_operand_x<D>(lds, vb, 1, 0);
+      f32x16 s, dp;
 #pragma unroll
-          for (int kk = 0; kk < KT; ++kk) {
-            bf16x8 q2 = q1, d2 = d1, v2 = v1;
-            if (kk + 2 < KT) {
-              q2 = row_operand_x<D>(lds, qb, kk + 2, 0);
-              d2 = row_operand_x<D>(lds, qb, kk + 2, C::Q_BYTES);
-              v2 = row_operand_x<D>(lds, vb, kk + 2, 0);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            if (kk == 0) {
-              s = mfma_v_first(q0, kB[0]);
-              dp = mfma_v_first(d0, v0);
-            } else {
-              mfma_v(s, q0, kB[kk]);
-              mfma_v(dp, d0, v0);
-            }
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      if (kind != 0) {
+        // S = Q K^T and dP = dO V^T into VGPRs (partial over this wave's half
+        // of the head dim when KDS = 2); the Q and dO (and V) row operands of
+        // k-step kk+2 are read before the MFMAs of step kk
+        bf16x8 q0 = row_operand_x<D>(lds, qb, 0, 0), d0 = row_operand_x<D>(lds, qb, 0, C::Q_BYTES);
+        bf16x8 q1 = row_operand_x<D>(lds, qb, 1, 0), d1 = row_operand_x<D>(lds, qb, 1, C::Q_BYTES);
+        bf16x8 v0 = KDS == 1 ? row_operand_x<D>(lds, vb, 0, 0) : vB[0];
+        bf16x8 v1 = KDS == 1 ? row_operand_x<D>(lds, vb, 1, 0) : vB[KDS == 1 ? 0 : 1];
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+          bf16x8 q2 = q1, d2 = d1, v2 = v1;
+          if (kk + 2 < KT) {
+            q2 = row_operand_x<D>(lds, qb, kk + 2, 0);
+            d2 = row_operand_x<D>(lds, qb, kk + 2, C::Q_BYTES);
+            if constexpr (KDS == 1) v2 = row_operand_x<D>(lds, vb, kk + 2, 0);
+            else v2 = vB[kk + 2 < KT ? kk + 2 : 0];
             __builtin_amdgcn_sched_barrier(0);
-            q0 = q1; q1 = q2;
-            d0 = d1; d1 = d2;
-            v0 = v1; v1 = v2;
           }
-          mfma_v_settle(s, dp);
+          if (kk == 0) {
+            s = mfma_v_first(q0, kB[0]);
+            dp = mfma_v_first(d0, v0);
+          } else {
+            mfma_v(s, q0, kB[kk]);
+            mfma_v(dp, d0, v0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          q0 = q1; q1 = q2;
+          d0 = d1; d1 = d2;
+          v0 = v1; v1 = v2;
         }
+        mfma_v_settle(s, dp);
+      }
+      if constexpr (KDS > 1) {
+        // partial S, then partial dP, of this half out and the partner's in,
+        // through one buffer (every wave, also on a skipped stage, so that
+        // the barriers are reached by all)
+        float4* xch = reinterpret_cast<float4*>(reinterpret_cast<char*>(lds) + C::XCH_REGION);
+        float4* xw = xch + wave_id * 4 * 64;
+        const float4* xp = xch + (wave_id ^ 1) * 4 * 64;
+        auto swap_in = [&](f32x16& a) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xw[j * 64 + lane] = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
+          block_sync();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 t = xp[j * 64 + lane];
+            a[4 * j] += t.x; a[4 * j + 1] += t.y; a[4 * j + 2] += t.z; a[4 * j + 3] += t.w;
+          }
+        };
+        swap_in(s);
+        block_sync();                        // every wave has read the S partials
+        swap_in(dp);
+      }
+      if (kind != 0) {
         if (kind == 2) {
           // query qc (+4*hf) of the stage is visible to this lane's key iff
           // 0 <= qpos - kpos < window and qc < nrows (branch-free); hidden
@@ -379,7 +426,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hf;
+        const int d = dh * DH + db * 32 + 8 * g4 + 4 * hf;
         float ak[4], av[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -413,11 +460,18 @@ hipError_t launch_bwd_dkdv_wide(const Problem& pr, const Groups& G, const KvGrou
                                 const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                                 const float* lse2, const float* delta, uint16_t* dk, uint16_t* dv, float* part_k,
                                 float* part_v, hipStream_t stream) {
-  if (pr.D != 256) return hipErrorInvalidValue;
   constexpr int NWK = 4, NS = 2;
-  static_assert(KvWideCfg<256, NWK, NS>::LDS_BYTES <= 160 * 1024, "LDS budget");
-  return launch("bwd_dkdv", bwd_dkdv_wide_kernel<256, NWK, NS>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream, pr,
-                G, kg, q, k, v, dout, lse2, delta, dk, dv, part_k, part_v);
+  if (pr.D == 256) {
+    static_assert(KvWideCfg<256, NWK, NS, 1>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<256, NWK, NS, 1>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
+                  pr, G, kg, q, k, v, dout, lse2, delta, dk, dv, part_k, part_v);
+  }
+  if (pr.D == 512) {
+    static_assert(KvWideCfg<512, NWK, NS, 2>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<512, NWK, NS, 2>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
+                  pr, G, kg, q, k, v, dout, lse2, delta, dk, dv, part_k, part_v);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dualkv

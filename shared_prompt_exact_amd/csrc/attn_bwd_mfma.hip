@@ -1030,7 +1030,7 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
   using CK = KvCfg<D, NWK, KVNS, KDS, VREG, KW>;
   static_assert(CK::LDS_BYTES <= 160 * 1024, "LDS budget");
   constexpr bool kv_lean = D == 128 && KDS == 1 && !VREG && KW == 1;
-  constexpr bool kv_wide = D == 256 && KDS == 1 && VREG && KW == 1 && NWK == 4;
+  constexpr bool kv_wide = ((D == 256 && KDS == 1) || (D == 512 && KDS == 2)) && VREG && KW == 1 && NWK == 4;
   if constexpr (!kv_lean && !kv_wide) {
     static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
     if (a2 != hipSuccess) return a2;

@@ -96,8 +96,8 @@ __device__ __forceinline__ void iter_next(const Problem& pr, StageIter& s, int k
   iter_fix(pr, s, kp_lo, kp_hi);
 }
 
-// dK/dV at head dim 256, one wave per SIMD with the accumulators in the
-// accumulation registers (attn_bwd_dkdv_wide.hip).
+// dK/dV at head dims 256 and 512, one wave per SIMD with the accumulators in
+// the accumulation registers (attn_bwd_dkdv_wide.hip).
 hipError_t launch_bwd_dkdv_wide(const Problem& pr, const Groups& G, const KvGroups& kg, int64_t nwg,
                                 const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                                 const float* lse2, const float* delta, uint16_t* dk, uint16_t* dv, float* part_k,
