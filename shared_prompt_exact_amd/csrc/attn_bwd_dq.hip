@@ -29,41 +29,35 @@ __device__ __forceinline__ int slot_value(int x) { return x; }
 
 // ----------------------------------------------------------------- dq kernel
 
-template <int D, int BN, int NW, int NS, int DS>
+template <int D, int BN, int NW, int NS>
 struct DqCfg {
   static constexpr int K_ELEMS = BN * D;         // swizzled row-major K tile
   static constexpr int V_ELEMS = BN * D;         // swizzled row-major V tile
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  // partial S and dP of a 32-key sub-tile: both at once, or (when LDS is
-  // short) S then dP through the same half-size buffer
-  static constexpr int XCH_FULL = DS > 1 ? NW * 64 * 32 * 4 : 0;
-  static constexpr bool XCH_TWO_PHASE = NS * STAGE * 2 + XCH_FULL > 160 * 1024;
-  static constexpr int XCH_BYTES = XCH_TWO_PHASE ? XCH_FULL / 2 : XCH_FULL;
-  static constexpr int LDS_BYTES = NS * STAGE * 2 + XCH_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE * 2;
   static constexpr int KBLK = BN * D * 2 / 1024;  // 1 KiB blocks per K (or V) tile
   static constexpr int BPW = KBLK / NW;
   static_assert(KBLK % NW == 0, "tile blocks must split evenly over the waves");
 };
 
-// DS = 2: a wave pair owns the same 32 query rows, each half of the head
-// dim (Q^T, dO^T, the contractions and the dQ accumulator); partial S and
-// dP meet in LDS and are summed in the same order by both waves.
-template <int D, int BN, int NW, int NS, int DS>
+// Head dims 64 and 128 (a wave holds whole rows: Q^T, dO^T and the dQ
+// accumulator of 32 query rows); 256 and 512 run attn_bwd_dq_wide.hip.
+template <int D, int BN, int NW, int NS>
 __global__ void __launch_bounds__(NW * 64)
     bwd_dq_kernel(Problem pa, Groups G, GroupBlocks GB, int HG, const uint16_t* __restrict__ q,
                   const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   const uint16_t* __restrict__ dout, const uint16_t* __restrict__ o,
                   const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ lse2w,
                   uint16_t* __restrict__ dq) {
-  using C = DqCfg<D, BN, NW, NS, DS>;
-  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32, K16 = BN / 16;
-  constexpr int KTH = KT / DS, DBH = DB / DS, NWQ = NW / DS;
+  using C = DqCfg<D, BN, NW, NS>;
+  static_assert(D <= 128, "whole rows per wave");
+  constexpr int KT = D / 16, NB32 = BN / 32, DB = D / 32;
   extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dh = wave % DS, wq = wave / DS;
-  const int BM = 32 * NWQ / HG;
+  const int wq = wave;
+  const int BM = 32 * NW / HG;
   const int NB = GB.off[G.n];                 // row blocks of all groups, per head group
   const int L = balanced_block(blockIdx.x, pa.Hq / HG, NB);
   if (L < 0) return;                          // grid padding (whole workgroup)
@@ -100,12 +94,12 @@ __global__ void __launch_bounds__(NW * 64)
   const bool w_any = w_hi >= wr0, w_all = wr0 + 31 < b.nvalid;
   const int wq_lo = b.posoff + wr0, wq_hi = b.posoff + w_hi;
 
-  bf16x8 qB[KTH], doB[KTH];
+  bf16x8 qB[KT], doB[KT];
 #pragma unroll
-  for (int kk = 0; kk < KTH; ++kk) {
+  for (int kk = 0; kk < KT; ++kk) {
     uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     if (qvalid) {
-      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * (dh * KTH + kk) + 8 * hf;
+      const int64_t off = qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf;
       z = *reinterpret_cast<const uint4*>(q + off);
       y = *reinterpret_cast<const uint4*>(dout + off);
     }
@@ -113,7 +107,7 @@ __global__ void __launch_bounds__(NW * 64)
     doB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   float lse2 = INFINITY, dlt = 0.f;   // +inf: p = 0 for rows without keys
-  if constexpr (DS == 1) {
+  {
     // Delta = dO . O of this row: the lane's half of the head dim (the same
     // elements as its dO^T operands), then the partner lane's half, added in
     // the same order in both lanes.  Written with LSE*log2(e) for the dK/dV
@@ -121,7 +115,7 @@ __global__ void __launch_bounds__(NW * 64)
     float part = 0.f;
     if (qvalid) {
 #pragma unroll
-      for (int kk = 0; kk < KTH; ++kk) {
+      for (int kk = 0; kk < KT; ++kk) {
         const bf16x8 ov = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(o + qrow * ostride + (int64_t)h * D + 16 * kk + 8 * hf));
 #pragma unroll
@@ -139,22 +133,17 @@ __global__ void __launch_bounds__(NW * 64)
       delta[(int64_t)h * pr.Tld + qrow] = dlt;
       lse2w[(int64_t)h * pr.Tld + qrow] = lse2;
     }
-  } else if (qvalid) {
-    const float Lr = lse[(int64_t)h * pr.Tld + qrow];
-    lse2 = Lr == -INFINITY ? INFINITY : Lr * kLog2e;
-    dlt = delta[(int64_t)h * pr.Tld + qrow];
   }
   wait_vmcnt<0>();                    // the loop's waits count only tile loads
   asm volatile("" ::: "memory");
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
 
-  f32x16 acc[DBH];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int db = 0; db < DBH; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float* const xch = reinterpret_cast<float*>(lds + NS * C::STAGE);   // DS > 1 only
 
   if (blk_hi >= b.r0) {
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
@@ -192,91 +181,25 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
         if (kind != 0) {
-          if constexpr (KTH <= 8) {
-            // the two operand reads of k-step kk+1 are issued before the
-            // two MFMAs of step kk (scheduling fences keep them there), so
-            // their latency overlaps MFMA work
-            bf16x8 ka = row_operand<D>(Ks, kb * 32 + l32, dh * KTH, hf);
-            bf16x8 va = row_operand<D>(Vs, kb * 32 + l32, dh * KTH, hf);
+          // the two operand reads of k-step kk+1 are issued before the two
+          // MFMAs of step kk (scheduling fences keep them there), so their
+          // latency overlaps MFMA work
+          bf16x8 ka = row_operand<D>(Ks, kb * 32 + l32, 0, hf);
+          bf16x8 va = row_operand<D>(Vs, kb * 32 + l32, 0, hf);
 #pragma unroll
-            for (int kk = 0; kk < KTH; ++kk) {
-              bf16x8 kn = ka, vn = va;
-              if (kk + 1 < KTH) {
-                kn = row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk + 1, hf);
-                vn = row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk + 1, hf);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-              s = mfma32(ka, qB[kk], s);
-              dp = mfma32(va, doB[kk], dp);
+          for (int kk = 0; kk < KT; ++kk) {
+            bf16x8 kn = ka, vn = va;
+            if (kk + 1 < KT) {
+              kn = row_operand<D>(Ks, kb * 32 + l32, kk + 1, hf);
+              vn = row_operand<D>(Vs, kb * 32 + l32, kk + 1, hf);
               __builtin_amdgcn_sched_barrier(0);
-              ka = kn;
-              va = vn;
             }
-          } else {
-#pragma unroll
-            for (int kk = 0; kk < KTH; ++kk) {
-              s = mfma32(row_operand<D>(Ks, kb * 32 + l32, dh * KTH + kk, hf), qB[kk], s);
-              dp = mfma32(row_operand<D>(Vs, kb * 32 + l32, dh * KTH + kk, hf), doB[kk], dp);
-              if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-            }
+            s = mfma32(ka, qB[kk], s);
+            dp = mfma32(va, doB[kk], dp);
+            __builtin_amdgcn_sched_barrier(0);
+            ka = kn;
+            va = vn;
           }
-        }
-        if constexpr (DS > 1) {
-          // partial S and dP of the DS waves sharing these rows meet in LDS;
-          // every wave adds the DS partials in index order (its own from
-          // registers), so all of them hold bit-identical sums.  Layout
-          // [wave][float4 j][lane]: each 16-byte access of a wave covers
-          // 1 KiB contiguous (no bank conflicts).  One phase: S in j = 0..3,
-          // dP in 4..7; two phases: S, then dP, in j = 0..3 of a buffer half
-          // the size.
-          float4* const x4 = reinterpret_cast<float4*>(xch);
-          constexpr int J = C::XCH_TWO_PHASE ? 4 : 8;
-          auto put = [&](const f32x16& a, int j0) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-              x4[(wave * J + j0 + i4) * 64 + lane] = make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
-          };
-          auto sum = [&](f32x16& a, int j0) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              float4 t4;
-              if constexpr (DS == 2) {
-                // own + partner: addition commutes, so both waves get the same bits
-                const float4 o4 = x4[((wave ^ 1) * J + j0 + i4) * 64 + lane];
-                t4 = make_float4(a[4 * i4] + o4.x, a[4 * i4 + 1] + o4.y, a[4 * i4 + 2] + o4.z, a[4 * i4 + 3] + o4.w);
-              } else {
-                // all DS partials, the own one included, read back and added in
-                // head-dim order by every wave
-                t4 = x4[((wave - dh) * J + j0 + i4) * 64 + lane];
-#pragma unroll
-                for (int pp = 1; pp < DS; ++pp) {
-                  const float4 v4 = x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
-                  t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
-                }
-              }
-              a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
-            }
-          };
-          if constexpr (C::XCH_TWO_PHASE) {
-            if (kind != 0) put(s, 0);
-            block_sync();
-            if (kind != 0) sum(s, 0);
-            block_sync();                       // every wave has read the S partials
-            if (kind != 0) put(dp, 0);
-            block_sync();
-            if (kind != 0) sum(dp, 0);
-          } else {
-            if (kind != 0) {
-              put(s, 0);
-              put(dp, 4);
-            }
-            block_sync();
-            if (kind != 0) {
-              sum(s, 0);
-              sum(dp, 4);
-            }
-          }
-          if (kb + 1 < NB32) block_sync();     // partials read before the next sub-tile's
         }
         if (kind != 0) {
           if (kind == 2) {
@@ -300,52 +223,37 @@ __global__ void __launch_bounds__(NW * 64)
               const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
               dsB[hs][j] = (__bf16)(p * (dp[i] - dlt));
             }
-          if constexpr (DBH <= 4) {
-            // k-step outer (independent accumulators back to back), each K^T
-            // operand read one MFMA ahead (scheduling fences hold the order)
-            bf16x8 cur = trans_operand<D>(Ks, 0, dh * DBH * 32, 2 * kb, lane);
+          // k-step outer (independent accumulators back to back), each K^T
+          // operand read one MFMA ahead (scheduling fences hold the order)
+          bf16x8 cur = trans_operand<D>(Ks, 0, 0, 2 * kb, lane);
 #pragma unroll
-            for (int x = 0; x < 2 * DBH; ++x) {
-              const int hs = x / DBH, db = x % DBH;
-              bf16x8 nxt = cur;
-              if (x + 1 < 2 * DBH) {
-                nxt = trans_operand<D>(Ks, 0, (dh * DBH + (x + 1) % DBH) * 32, 2 * kb + (x + 1) / DBH, lane);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-              acc[db] = mfma32(cur, dsB[hs], acc[db]);
+          for (int x = 0; x < 2 * DB; ++x) {
+            const int hs = x / DB, db = x % DB;
+            bf16x8 nxt = cur;
+            if (x + 1 < 2 * DB) {
+              nxt = trans_operand<D>(Ks, 0, ((x + 1) % DB) * 32, 2 * kb + (x + 1) / DB, lane);
               __builtin_amdgcn_sched_barrier(0);
-              cur = nxt;
             }
-          } else {
-#pragma unroll
-            for (int db = 0; db < DBH; ++db) {
-#pragma unroll
-              for (int hs = 0; hs < 2; ++hs)
-                acc[db] = mfma32(trans_operand<D>(Ks, 0, (dh * DBH + db) * 32, 2 * kb + hs, lane), dsB[hs],
-                                 acc[db]);
-              if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-            }
+            acc[db] = mfma32(cur, dsB[hs], acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
           }
         }
       }
     };
     static_assert(NS >= 2 && NS <= 4, "ring depth");
-    if constexpr (D <= 128) {
-      // unrolled by the ring depth (small head dims: registers to spare)
-      int it = 0;
-      for (; it + NS <= ntiles; it += NS) {
-        step(it, IntC<0>{});
-        step(it + 1, IntC<1>{});
-        if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
-        if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
-      }
-      if (it < ntiles) step(it, IntC<0>{});
-      if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
-      if constexpr (NS == 4)
-        if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
-    } else {
-      for (int it = 0; it < ntiles; ++it) step(it, it % NS);
+    // unrolled by the ring depth
+    int it = 0;
+    for (; it + NS <= ntiles; it += NS) {
+      step(it, IntC<0>{});
+      step(it + 1, IntC<1>{});
+      if constexpr (NS >= 3) step(it + 2, IntC<2 % NS>{});
+      if constexpr (NS == 4) step(it + 3, IntC<3 % NS>{});
     }
+    if (it < ntiles) step(it, IntC<0>{});
+    if (it + 1 < ntiles) step(it + 1, IntC<1 % NS>{});
+    if constexpr (NS == 4)
+      if (it + 2 < ntiles) step(it + 2, IntC<2 % NS>{});
   }
 
   // the row and half of this lane are formed again from the lane index
@@ -355,13 +263,13 @@ __global__ void __launch_bounds__(NW * 64)
   if (e_r < b.seglen) {
     uint16_t* orow = dq + ((int64_t)b.base + e_r) * ostride + (int64_t)h * D;
 #pragma unroll
-    for (int db = 0; db < DBH; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         union { __bf16 h[4]; uint2 u; } pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk.h[e] = (__bf16)(acc[db][4 * g4 + e] * pr.scale);
-        *reinterpret_cast<uint2*>(orow + (dh * DBH + db) * 32 + 8 * g4 + 4 * e_hf) = pk.u;
+        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g4 + 4 * e_hf) = pk.u;
       }
   }
 }
@@ -369,25 +277,25 @@ __global__ void __launch_bounds__(NW * 64)
 
 }  // namespace
 
-template <int D, int BN, int NW, int NS, int DS>
+template <int D, int BN, int NW, int NS>
 hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
                          const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                          const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
                          hipStream_t stream) {
-  using C = DqCfg<D, BN, NW, NS, DS>;
+  using C = DqCfg<D, BN, NW, NS>;
   static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = allow_lds(bwd_dq_kernel<D, BN, NW, NS, DS>, C::LDS_BYTES);
+  static const hipError_t attr = allow_lds(bwd_dq_kernel<D, BN, NW, NS>, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  return launch("bwd_dq", bwd_dq_kernel<D, BN, NW, NS, DS>, dim3((unsigned)nwg), dim3(NW * 64), C::LDS_BYTES,
+  return launch("bwd_dq", bwd_dq_kernel<D, BN, NW, NS>, dim3((unsigned)nwg), dim3(NW * 64), C::LDS_BYTES,
                 stream, pr, G, gb, HG, q, k, v, dout, o, lse, delta, lse2, dq);
 }
 
 // the configurations the backward dispatch uses
-template hipError_t launch_bwd_dq<64, 64, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+template hipError_t launch_bwd_dq<64, 64, 8, 3>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                    const uint16_t*, const uint16_t*, const uint16_t*,
                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                    uint16_t*, hipStream_t);
-template hipError_t launch_bwd_dq<128, 32, 8, 3, 1>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+template hipError_t launch_bwd_dq<128, 32, 8, 3>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);

@@ -37,439 +37,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // --------------------------------------------------------------- dkdv kernel
 
-template <int D, int NWK, int NS, int DS, bool VREG, int KW>
+template <int D, int NWK, int NS>
 struct KvCfg {
-  static constexpr int BK = 32 * KW * NWK / DS;     // keys per workgroup
-  static constexpr int V_ELEMS = VREG ? 0 : BK * D; // V tile (B operand of dP), loaded once
+  static constexpr int BK = 32 * NWK;               // keys per workgroup
+  static constexpr int V_ELEMS = BK * D;            // V tile (B operand of dP), loaded once
   static constexpr int Q_ELEMS = kStageRows * D;    // Q stage rows
   static constexpr int DO_ELEMS = kStageRows * D;   // dO stage rows
   static constexpr int STAT = 2 * kStageRows * 2;   // LSE and delta, fp32 (in u16 units)
   static constexpr int STAGE = Q_ELEMS + DO_ELEMS + STAT;
-  // partial S and dP of the head-dim split: both at once, or (when LDS is
-  // short) S then dP through the same half-size buffer
-  static constexpr int XCH_FULL = DS > 1 ? NWK * 64 * 32 * 4 : 0;
-  static constexpr bool XCH_TWO_PHASE = (V_ELEMS + NS * STAGE) * 2 + XCH_FULL > 160 * 1024;
-  static constexpr int XCH_BYTES = XCH_TWO_PHASE ? XCH_FULL / 2 : XCH_FULL;
-  static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2 + XCH_BYTES;
+  static constexpr int LDS_BYTES = (V_ELEMS + NS * STAGE) * 2;
   static constexpr int VBPW = V_ELEMS * 2 / 1024 / NWK;     // V blocks per wave
   static constexpr int QBLK = Q_ELEMS * 2 / 1024;           // blocks per Q (or dO) stage tile
   static constexpr int SBPW = 2 * QBLK / NWK;               // stage blocks per wave
   static_assert(V_ELEMS * 2 % (1024 * NWK) == 0 && 2 * QBLK % NWK == 0, "even split");
 };
 
-// DS = 2: a wave pair owns the same 32 keys, each half of the head dim (K^T
-// and V^T operands, the S / dP contractions and the dK / dV accumulators);
-// partial S and dP meet in LDS.  VREG keeps V^T in registers instead of a
-// V tile in LDS (large head dims, where LDS is short).  KW = 2: a wave owns
-// two 32-key tiles (one wave per SIMD, the dK / dV accumulators in the
-// accumulation registers), so each Q, dO, Q^T, dO^T operand read from LDS
-// feeds two MFMAs.
-template <int D, int NWK, int NS, int DS, bool VREG, int KW>
-__global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1, KW == 2 ? 1 : 8)))
-    bwd_dkdv_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
-                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                    const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
-                    const float* __restrict__ delta, uint16_t* __restrict__ dk,
-                    uint16_t* __restrict__ dv, float* __restrict__ part_k,
-                    float* __restrict__ part_v) {
-  using C = KvCfg<D, NWK, NS, DS, VREG, KW>;
-  constexpr int KT = D / 16, DB = D / 32, KTH = KT / DS, DBH = DB / DS;
-  static_assert(KW == 1 || (DS == 1 && !VREG), "two key tiles per wave: no head-dim split");
-  extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  // ---- decode the work item (groups in order, longest first within a
-  // group and KV head)
-  const int per_head = KG.off[G.n];
-  const int Lid = balanced_block(blockIdx.x, pa.Hkv, per_head);
-  if (Lid < 0) return;                        // grid padding (whole workgroup)
-  KvItem it;
-  it.c = Lid / per_head;
-  int x = Lid % per_head;
-  const int gi = order_lookup(KG.ord, x, x);
-  const Problem pr = group_problem(pa, G, gi);
-  const KvShape sh = KG.sh[gi];
-  {
-    const int64_t r0 = G.row0[gi];
-    q += r0 * pr.Hq * D;
-    dout += r0 * pr.Hq * D;
-    k += r0 * pr.Hkv * D;
-    v += r0 * pr.Hkv * D;
-    dk += r0 * pr.Hkv * D;
-    dv += r0 * pr.Hkv * D;
-    lse2 += r0;
-    delta += r0;
-    part_k += KG.part[gi];
-    part_v += KG.part[gi];
-  }
-  // response slots exist only for prompt tiles t0 .. nPt-1 (all of them
-  // without a window)
-  const int nPtR = sh.nPt - sh.t0;
-  if (x < nPtR * (sh.slots - 1) + sh.nPt) {
-    it.seg = -1;
-    if (x < nPtR * (sh.slots - 1)) {                      // response slots first
-      it.slot = 1 + x / nPtR;
-      it.k0 = (sh.t0 + x % nPtR) * C::BK;
-    } else {                                              // then the prompt slot
-      it.slot = 0;
-      it.k0 = (x - nPtR * (sh.slots - 1)) * C::BK;
-    }
-  } else {
-    x -= nPtR * (sh.slots - 1) + sh.nPt;
-    it.seg = x % pr.N;
-    it.k0 = (x / pr.N) * C::BK;
-    it.slot = 0;
-  }
-  const int c = it.c;
-  const int seg_base = it.seg < 0 ? 0 : pr.P + it.seg * pr.R;
-  const int seg_valid = it.seg < 0 ? pr.P : resp_valid(pr, it.seg);
-  const int seg_len = it.seg < 0 ? pr.P : pr.R;
-  const int posoff = it.seg < 0 ? 0 : pr.P;
-  const int klim = seg_valid - it.k0;                 // valid keys of the tile
-  const int kp_lo = posoff + it.k0;
-  const int kp_hi = posoff + it.k0 + min(C::BK, max(klim, 1)) - 1;
-
-  // ---- this wave's 32*KW keys: K^T as B operands in registers; the V
-  // tile row-major in LDS (B operand of dP).  With K only in registers a
-  // wave of one key tile fits in 256 registers and two waves share each SIMD.
-  const int dh = wave % DS;                           // head-dim half of this wave
-  const int wk0 = 32 * KW * (wave / DS);              // first key of the wave in the tile
-  int my_k[KW], kpos[KW];
-  bool kvalid[KW];
-  int64_t krow[KW];
-  const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KW][KTH], vB[VREG ? KTH : 1];
-#pragma unroll
-  for (int kt = 0; kt < KW; ++kt) {
-    my_k[kt] = wk0 + 32 * kt + l32;
-    kvalid[kt] = my_k[kt] < klim;
-    kpos[kt] = kp_lo + my_k[kt];
-    krow[kt] = (int64_t)seg_base + it.k0 + my_k[kt];
-#pragma unroll
-    for (int kk = 0; kk < KTH; ++kk) {
-      uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-      const int64_t off = krow[kt] * kstride + (int64_t)c * D + 16 * (dh * KTH + kk) + 8 * hf;
-      if (kvalid[kt]) {
-        z = *reinterpret_cast<const uint4*>(k + off);
-        if constexpr (VREG) y = *reinterpret_cast<const uint4*>(v + off);
-      }
-      kB[kt][kk] = __builtin_bit_cast(bf16x8, z);
-      if constexpr (VREG) vB[kk] = __builtin_bit_cast(bf16x8, y);
-    }
-  }
-  wait_vmcnt<0>();                    // the loop's waits count only LDS loads
-  asm volatile("" ::: "memory");
-  const uint16_t* Vs = lds;
-  uint16_t* const stage_base = lds + C::V_ELEMS;
-  if (!VREG && klim > 0)
-    dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride,
-                min(C::BK, klim), lds, wave * C::VBPW, C::VBPW, lane);
-  float* const xch = reinterpret_cast<float*>(stage_base + NS * C::STAGE);   // DS > 1 only
-  const int wk_valid = min(32 * KW, klim - wk0);      // valid keys of this wave
-  const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
-
-  f32x16 dKt[DBH][KW], dVt[DBH][KW];
-#pragma unroll
-  for (int db = 0; db < DBH; ++db)
-#pragma unroll
-    for (int kt = 0; kt < KW; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dKt[db][kt][i] = dVt[db][kt][i] = 0.f;
-
-  // ---- the query stages of this item, NS-1 stages ahead in an LDS ring
-  StageIter s0;
-  if (it.seg >= 0) {
-    s0.seg = s0.seg_last = it.seg;
-  } else if (it.slot == 0) {
-    s0.seg = s0.seg_last = -1;
-  } else {
-    s0.seg = (it.slot - 1) * sh.per_slot;
-    s0.seg_last = min(pr.N, it.slot * sh.per_slot) - 1;
-  }
-  s0.h0 = s0.h = c * pr.g;
-  s0.h1 = (c + 1) * pr.g;
-  s0.r = 0;
-  s0.ok = false;
-  if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
-  StageIter s1 = s0;
-  if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
-  // NS == 3: stages s0, s1 in flight, s2 issued after the barrier;
-  // NS == 2: s0 in flight, s1 issued after the barrier;
-  // NS == 1: s1 issued once every wave is done with the single buffer.
-  static_assert(NS >= 1 && NS <= 3, "stage ring depth");
-  StageIter s2 = s1;
-  if (NS == 3 && s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
-
-  const int64_t qstride = (int64_t)pr.Hq * D;
-  const float c2 = pr.scale * kLog2e;
-  const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
-  const bool stat_wave = wave == NWK - 1;    // also loads the stage's lse2 / delta
-
-  auto issue = [&](const StageIter& st, int slot) {
-    const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
-    const int n = min(kStageRows, st.svalid - st.r);
-    const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
-    uint16_t* buf = stage_base + slot * C::STAGE;
-    // blocks w, w + NWK, ... of [Q blocks, dO blocks]
-#pragma unroll
-    for (int j = 0; j < C::SBPW; ++j) {
-      const int blk = wave + j * NWK;
-      if (blk < C::QBLK) dma_rows<D>(q + off, qstride, n, buf, blk, 1, lane);
-      else dma_rows<D>(dout + off, qstride, n, buf + C::Q_ELEMS, blk - C::QBLK, 1, lane);
-    }
-    if (stat_wave) {
-      // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
-      const int row = sb + st.r + min(lane & 31, n - 1);
-      const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.Tld + row;
-      const unsigned ldsaddr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(
-          __attribute__((address_space(3))) void*)(buf + C::Q_ELEMS + C::DO_ELEMS));
-      asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
-    }
-  };
-
-  int idx = 0;
-  if (s0.ok) issue(s0, 0);
-  if (NS == 3 && s1.ok) issue(s1, 1);
-  while (s0.ok) {
-    // stage s0 (and the V tile) landed once only s1's loads may be pending
-    if (NS == 3 && s1.ok) {
-      if (stat_wave) wait_vmcnt<C::SBPW + 1>();
-      else wait_vmcnt<C::SBPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    block_sync();
-    if (NS == 3) {
-      if (s2.ok) issue(s2, (idx + 2) % NS);
-    } else if (NS == 2) {
-      if (s1.ok) issue(s1, (idx + 1) % NS);
-    }
-    {
-      const uint16_t* Qs = stage_base + (idx % NS) * C::STAGE;
-      const uint16_t* DOs = Qs + C::Q_ELEMS;
-      const float* stat = reinterpret_cast<const float*>(DOs + C::DO_ELEMS);
-      const int s_posoff = s0.seg < 0 ? 0 : pr.P;
-      const int nrows = min(kStageRows, s0.svalid - s0.r);
-      const int sq_lo = s_posoff + s0.r, sq_hi = sq_lo + nrows - 1;
-      // skip / full / masked for this wave's keys against the stage's queries
-      int kind;
-      if (wk_valid <= 0 || nrows <= 0 || sq_hi < wkp_lo || (pr.W > 0 && sq_lo - wkp_hi >= pr.W)) kind = 0;
-      else if (wk_valid == 32 * KW && nrows == kStageRows && sq_lo >= wkp_hi &&
-               (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
-      else kind = 2;
-      f32x16 s[KW], dp[KW];
-#pragma unroll
-      for (int kt = 0; kt < KW; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kt][i] = dp[kt][i] = 0.f;
-      if (kind != 0) {
-        if constexpr (KW == 1 && !VREG && KTH <= 8) {
-          // the operand reads of k-step kk+1 are issued before the two
-          // MFMAs of step kk (scheduling fences keep them there)
-          const int kc0 = dh * KTH;
-          bf16x8 qa = row_operand<D>(Qs, l32, kc0, hf), da = row_operand<D>(DOs, l32, kc0, hf);
-          bf16x8 vb = row_operand<D>(Vs, wk0 + l32, kc0, hf);
-#pragma unroll
-          for (int kk = 0; kk < KTH; ++kk) {
-            bf16x8 qn = qa, dn = da, vn = vb;
-            if (kk + 1 < KTH) {
-              qn = row_operand<D>(Qs, l32, kc0 + kk + 1, hf);
-              dn = row_operand<D>(DOs, l32, kc0 + kk + 1, hf);
-              vn = row_operand<D>(Vs, wk0 + l32, kc0 + kk + 1, hf);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            s[0] = mfma32(qa, kB[0][kk], s[0]);
-            dp[0] = mfma32(da, vb, dp[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            qa = qn;
-            da = dn;
-            vb = vn;
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < KTH; ++kk) {
-            const int kc = dh * KTH + kk;
-            const bf16x8 qa = row_operand<D>(Qs, l32, kc, hf);
-            const bf16x8 da = row_operand<D>(DOs, l32, kc, hf);
-#pragma unroll
-            for (int kt = 0; kt < KW; ++kt) {
-              const bf16x8 vb = VREG ? vB[VREG ? kk : 0] : row_operand<D>(Vs, wk0 + 32 * kt + l32, kc, hf);
-              s[kt] = mfma32(qa, kB[kt][kk], s[kt]);
-              dp[kt] = mfma32(da, vb, dp[kt]);
-            }
-            if constexpr (KTH > 8) if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      if constexpr (DS > 1) {
-        // partial S and dP of the DS waves sharing these keys meet in LDS
-        // (all of them share `kind`); summed in index order by every wave
-        // layout [wave][float4 j][lane]: each 16-byte access of a wave covers
-        // 1 KiB contiguous.  One phase: S in j = 0..3, dP in 4..7; two
-        // phases: S, then dP, in j = 0..3 of a buffer half the size.
-        float4* const x4 = reinterpret_cast<float4*>(xch);
-        constexpr int J = C::XCH_TWO_PHASE ? 4 : 8;
-        auto put = [&](const f32x16& a, int j0) {
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4)
-            x4[(wave * J + j0 + i4) * 64 + lane] = make_float4(a[4 * i4], a[4 * i4 + 1], a[4 * i4 + 2], a[4 * i4 + 3]);
-        };
-        auto sum = [&](f32x16& a, int j0) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              float4 t4;
-              if constexpr (DS == 2) {
-                // own + partner: addition commutes, so both waves get the same bits
-                const float4 o4 = x4[((wave ^ 1) * J + j0 + i4) * 64 + lane];
-                t4 = make_float4(a[4 * i4] + o4.x, a[4 * i4 + 1] + o4.y, a[4 * i4 + 2] + o4.z, a[4 * i4 + 3] + o4.w);
-              } else {
-                // all DS partials, the own one included, read back and added in
-                // head-dim order by every wave
-                t4 = x4[((wave - dh) * J + j0 + i4) * 64 + lane];
-#pragma unroll
-                for (int pp = 1; pp < DS; ++pp) {
-                  const float4 v4 = x4[((wave - dh + pp) * J + j0 + i4) * 64 + lane];
-                  t4.x += v4.x; t4.y += v4.y; t4.z += v4.z; t4.w += v4.w;
-                }
-              }
-              a[4 * i4] = t4.x; a[4 * i4 + 1] = t4.y; a[4 * i4 + 2] = t4.z; a[4 * i4 + 3] = t4.w;
-            }
-          };
-        if constexpr (C::XCH_TWO_PHASE) {
-          if (kind != 0) put(s[0], 0);
-          block_sync();
-          if (kind != 0) sum(s[0], 0);
-          block_sync();                       // every wave has read the S partials
-          if (kind != 0) put(dp[0], 0);
-          block_sync();
-          if (kind != 0) sum(dp[0], 0);
-        } else {
-          if (kind != 0) {
-            put(s[0], 0);
-            put(dp[0], 4);
-          }
-          block_sync();
-          if (kind != 0) {
-            sum(s[0], 0);
-            sum(dp[0], 4);
-          }
-        }
-      }
-      if (kind != 0) {
-        bf16x8 pB[KW][2], dsB[KW][2];
-        if (kind == 2) {
-          // query qc (+4*hf) of the stage is visible to this lane's key iff
-          // 0 <= qpos - kpos < window and qc < nrows (branch-free); hidden
-          // scores become -inf, so p = exp2(-inf - lse2) = 0 below.
-#pragma unroll
-          for (int kt = 0; kt < KW; ++kt) {
-            int e0 = sq_lo + 4 * hf - kpos[kt];
-            int n0 = (kvalid[kt] ? nrows : 0) - 4 * hf;
-            asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int qc = 8 * (i >> 2) + (i & 3);           // query row - 4*hf
-              const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
-              s[kt][i] = vis ? s[kt][i] : -INFINITY;
-            }
-          }
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(stat + 8 * g4 + 4 * hf);
-          const float4 d4 = *reinterpret_cast<const float4*>(stat + kStageRows + 8 * g4 + 4 * hf);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;                       // register index
-#pragma unroll
-            for (int kt = 0; kt < KW; ++kt) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -lv[e]));
-              const float ds = p * (dp[kt][i] - dv4[e]);
-              pB[kt][i >> 3][i & 7] = (__bf16)p;
-              dsB[kt][i >> 3][i & 7] = (__bf16)ds;
-            }
-          }
-        }
-#pragma unroll
-        for (int db = 0; db < DBH; ++db) {
-          const int col = (dh * DBH + db) * 32;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 da = trans_operand<D>(DOs, 0, col, ks, lane);
-            const bf16x8 qa = trans_operand<D>(Qs, 0, col, ks, lane);
-#pragma unroll
-            for (int kt = 0; kt < KW; ++kt) {
-              dVt[db][kt] = mfma32(da, pB[kt][ks], dVt[db][kt]);
-              dKt[db][kt] = mfma32(qa, dsB[kt][ks], dKt[db][kt]);
-            }
-          }
-          if constexpr (DBH > 4) if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    if (NS == 1) {
-      block_sync();                        // every wave is done with the buffer
-      if (s1.ok) issue(s1, 0);
-    }
-    s0 = s1;
-    if (NS == 3) {
-      s1 = s2;
-      if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
-    } else if (s1.ok) {
-      iter_next(pr, s1, kp_lo, kp_hi);
-    }
-    ++idx;
-  }
-
-  // ---- write dK (scaled) and dV for this lane's keys
-  // prompt tiles with response slots write fp32 partials for the reduction
-  const bool partial = it.seg < 0 && sh.slots > 1 && it.k0 >= sh.t0 * C::BK;
-#pragma unroll
-  for (int kt = 0; kt < KW; ++kt) {
-    if (my_k[kt] < seg_len - it.k0) {
-#pragma unroll
-      for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = (dh * DBH + db) * 32 + 8 * g4 + 4 * hf;
-          const f32x16& ak = dKt[db][kt];
-          const f32x16& av = dVt[db][kt];
-          if (partial) {
-            // partials cover prompt rows t0*BK .. P-1 only: [slots, P - t0*BK, Hkv, D]
-            const int prow0 = sh.t0 * C::BK;
-            const int64_t o =
-                (((int64_t)it.slot * (pr.P - prow0) + it.k0 + my_k[kt] - prow0) * pr.Hkv + c) * D + d;
-            *reinterpret_cast<float4*>(part_k + o) =
-                make_float4(ak[4 * g4] * pr.scale, ak[4 * g4 + 1] * pr.scale, ak[4 * g4 + 2] * pr.scale,
-                            ak[4 * g4 + 3] * pr.scale);
-            *reinterpret_cast<float4*>(part_v + o) =
-                make_float4(av[4 * g4], av[4 * g4 + 1], av[4 * g4 + 2], av[4 * g4 + 3]);
-          } else {
-            const int64_t o = krow[kt] * kstride + (int64_t)c * D + d;
-            union { __bf16 h[4]; uint2 u; } pk, pv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pk.h[e] = (__bf16)(ak[4 * g4 + e] * pr.scale);
-              pv.h[e] = (__bf16)av[4 * g4 + e];
-            }
-            *reinterpret_cast<uint2*>(dk + o) = pk.u;
-            *reinterpret_cast<uint2*>(dv + o) = pv.u;
-          }
-        }
-    }
-  }
-}
-
-// The dK/dV kernel above for head dim 128 (a wave holds whole rows, one
-// 32-key tile per wave, V in LDS), with cheaper addressing: a statically
-// sized LDS block (V tile, then NS query stages), operand addresses derived
-// from a few per-lane bases with one XOR per 16-byte chunk and immediate
-// tile offsets (lds_tiles.h), and stage loads from a scalar row address
-// plus one per-lane offset fixed for the kernel (rows clamped only on a
-// partial stage).  Same work items, schedule and arithmetic.
+// dK/dV at head dims 64 and 128: a wave owns 32 keys (K^T as B operands in
+// registers) and holds whole rows; the item's V tile sits row-major in a
+// statically sized LDS block, then NS query stages (Q, dO row-major with
+// their lse2 / delta).  Operand addresses come from a few per-lane bases
+// with one XOR per 16-byte chunk and immediate tile offsets (lds_tiles.h);
+// stage loads take a scalar row address plus per-lane offsets fixed for the
+// kernel (rows clamped only on a partial stage).
 template <int D, int NWK, int NS>
 __global__ void __launch_bounds__(NWK * 64)
     bwd_dkdv_lean_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
@@ -478,7 +67,7 @@ __global__ void __launch_bounds__(NWK * 64)
                          const float* __restrict__ delta, uint16_t* __restrict__ dk,
                          uint16_t* __restrict__ dv, float* __restrict__ part_k,
                          float* __restrict__ part_v) {
-  using C = KvCfg<D, NWK, NS, 1, false, 1>;
+  using C = KvCfg<D, NWK, NS>;
   constexpr int KT = D / 16, DB = D / 32, BK = C::BK;
   constexpr unsigned V_BYTES = C::V_ELEMS * 2, Q_BYTES = C::Q_ELEMS * 2, DO_BYTES = C::DO_ELEMS * 2;
   constexpr unsigned STAGE_BYTES = C::STAGE * 2;
@@ -873,19 +462,15 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------------ planning
 
-// Waves per workgroup and head-dim split (DS waves share rows, each with
-// D/DS dims of state): two waves per SIMD up to D = 128, one above.  Both
-// kernels split the head dim in two only at D = 512: a wave then holds at
-// most 256 dims of its operands and accumulators (VGPRs plus accumulation
-// registers), and the waves of a workgroup cover several 32-row (or
-// 32-key) slices that share each streamed tile.
+// Waves per workgroup and head-dim split (DS waves share rows or keys, each
+// with D/DS dims of state).  Up to D = 128 the kernels run two (or more)
+// waves per SIMD; at 256 and 512 one, with the accumulators in the
+// accumulation registers (attn_bwd_dq_wide.hip, attn_bwd_dkdv_wide.hip), and
+// at 512 a wave pair splits the head dim, so that a wave holds at most 256
+// dims of its operands and accumulators.  The dK/dV kernel at head dim 64
+// runs four waves (one 32-row Q and dO block per wave and stage).
 inline int dq_waves(int D) { return D >= 256 ? 4 : 8; }
-inline int kv_waves(int D) { return D <= 128 ? 8 : 4; }
-// Key tiles per wave of the dK/dV kernel.  Two tiles (one wave per SIMD)
-// halve the LDS reads per MFMA but lose the second wave's latency hiding;
-// measured slower at D = 128 (11.6 ms against 9.9 ms on the Qwen3-8B-shaped
-// layer), so every head dim runs one tile per wave.
-inline int kv_tiles_per_wave(int) { return 1; }
+inline int kv_waves(int D) { return D == 128 ? 8 : 4; }
 inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
 inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
@@ -964,7 +549,7 @@ BwdPlan plan(const Problem& pr, const Groups& G) {
   p.DS = dq_split(pr.D);
   p.HG = heads_per_block(pr.g, p.NW / p.DS);
   p.BM = 32 * (p.NW / p.DS) / p.HG;
-  const int BK = 32 * kv_tiles_per_wave(pr.D) * kv_waves(pr.D) / kv_split(pr.D);
+  const int BK = 32 * kv_waves(pr.D) / kv_split(pr.D);
   p.BK = BK;
   constexpr int64_t kBig = INT32_MAX;
   int64_t nb = 0, items = 0, part = 0, red = 0;
@@ -1023,18 +608,14 @@ BwdPlan plan(const Problem& pr, const Groups& G) {
   return p;
 }
 
-template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS, int KDS, bool VREG, int KW>
+template <int D, int NW, int NWK, int kDqBN, int DQNS, int KVNS, int DS>
 hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void* q, const void* k, const void* v,
                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                char* ws, hipStream_t stream) {
-  using CK = KvCfg<D, NWK, KVNS, KDS, VREG, KW>;
-  static_assert(CK::LDS_BYTES <= 160 * 1024, "LDS budget");
-  constexpr bool kv_lean = D == 128 && KDS == 1 && !VREG && KW == 1;
-  constexpr bool kv_wide = ((D == 256 && KDS == 1) || (D == 512 && KDS == 2)) && VREG && KW == 1 && NWK == 4;
-  if constexpr (!kv_lean && !kv_wide) {
-    static const hipError_t a2 = allow_lds(bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, CK::LDS_BYTES);
-    if (a2 != hipSuccess) return a2;
-  }
+  // dK/dV: the LDS-staged kernel above up to D = 128, the kernel with its
+  // accumulators in the accumulation registers above (own translation unit)
+  constexpr bool kv_lean = D <= 128;
+  static_assert(!kv_lean || KvCfg<D, NWK, KVNS>::LDS_BYTES <= 160 * 1024, "LDS budget");
   float* delta = reinterpret_cast<float*>(ws + p.off_delta);
   float* lse2 = reinterpret_cast<float*>(ws + p.off_lse2);
   float* pk = reinterpret_cast<float*>(ws + p.off_pk);
@@ -1054,13 +635,13 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
     if (e != hipSuccess) return e;
   }
   if (p.nwg_dq > 0) {
-    if constexpr ((D == 256 && DS == 1 && NW == 4) || (D == 512 && DS == 2 && NW == 4))
+    if constexpr (D >= 256)
       e = launch_bwd_dq_wide(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16, static_cast<const uint16_t*>(o),
                              lse, delta, lse2, static_cast<uint16_t*>(dq), stream);
     else
-      e = launch_bwd_dq<D, kDqBN, NW, DQNS, DS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16,
-                                                 static_cast<const uint16_t*>(o), lse, delta, lse2,
-                                                 static_cast<uint16_t*>(dq), stream);
+      e = launch_bwd_dq<D, kDqBN, NW, DQNS>(pr, G, p.gb, p.HG, p.nwg_dq, q16, k16, v16, do16,
+                                             static_cast<const uint16_t*>(o), lse, delta, lse2,
+                                             static_cast<uint16_t*>(dq), stream);
     if (e != hipSuccess) return e;
   }
   if (p.nwg_kv > 0) {
@@ -1068,13 +649,9 @@ hipError_t run(const Problem& pr, const Groups& G, const BwdPlan& p, const void*
       e = launch("bwd_dkdv", bwd_dkdv_lean_kernel<D, NWK, KVNS>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64), 0,
                  stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                  static_cast<uint16_t*>(dv), pk, pv);
-    else if constexpr (kv_wide)
+    else
       e = launch_bwd_dkdv_wide(pr, G, p.kg, p.nwg_kv, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
                                static_cast<uint16_t*>(dv), pk, pv, stream);
-    else
-      e = launch("bwd_dkdv", bwd_dkdv_kernel<D, NWK, KVNS, KDS, VREG, KW>, dim3((unsigned)p.nwg_kv), dim3(NWK * 64),
-                 CK::LDS_BYTES, stream, pr, G, p.kg, q16, k16, v16, do16, lse2, delta, static_cast<uint16_t*>(dk),
-                 static_cast<uint16_t*>(dv), pk, pv);
     if (e != hipSuccess) return e;
   }
   if (p.reduce) {
@@ -1101,11 +678,11 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   const BwdPlan p = plan(pr, G);
   char* ws = static_cast<char*>(workspace);
   switch (pr.D) {
-    //                D  NW NWK BN DQNS KVNS DS KDS VREG KW
-    case 64: return run<64, 8, 8, 64, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, 8, 32, 3, 3, 1, 1, false, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 256: return run<256, 4, 4, 32, 3, 3, 1, 1, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 512: return run<512, 4, 4, 32, 2, 2, 2, 2, true, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    //                D  NW NWK BN DQNS KVNS DS
+    case 64: return run<64, 8, 4, 64, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 8, 8, 32, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 256: return run<256, 4, 4, 32, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 512: return run<512, 4, 4, 32, 2, 2, 2>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -232,12 +232,12 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
                            const void* v, const void* o, const float* lse, const void* dout,
                            void* dq, void* dk, void* dv, void* workspace, hipStream_t stream);
 
-// dQ kernel of the MFMA backward (attn_bwd_dq.hip), for the configurations
-// the dispatch in attn_bwd_mfma.hip uses.  With DS == 1 (a wave holds whole
-// rows) the kernel also forms Delta = rowsum(dO*O) of its rows and writes it
-// with LSE*log2(e) (+inf where LSE = -inf) to `delta` and `lse2`; with
-// DS > 1 it reads `delta`, written beforehand by the Delta kernel.
-template <int D, int BN, int NW, int NS, int DS>
+// dQ kernel of the MFMA backward at head dims 64 and 128 (attn_bwd_dq.hip),
+// for the configurations the dispatch in attn_bwd_mfma.hip uses.  A wave
+// holds whole rows; the kernel also forms Delta = rowsum(dO*O) of its rows
+// and writes it with LSE*log2(e) (+inf where LSE = -inf) to `delta` and
+// `lse2`.
+template <int D, int BN, int NW, int NS>
 hipError_t launch_bwd_dq(const Problem& pr, const Groups& G, const GroupBlocks& gb, int HG, int64_t nwg,
                          const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                          const uint16_t* o, const float* lse, float* delta, float* lse2, uint16_t* dq,
