@@ -40,9 +40,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 # library kernel name -> (substrings of the device symbols, source files they are built from)
 _HEADERS = ["common.h", "mfma_common.h", "lds_tiles.h"]
 KERNELS = {
-    "fwd": (("fwd_mfma_kernel", "fwd_lean_kernel"), ["attn_fwd_mfma.hip"] + _HEADERS),
-    "bwd_dq": (("bwd_dq_kernel", "bwd_dq_lean_kernel", "bwd_dq_wide_kernel"), ["attn_bwd_dq.hip", "attn_bwd_dq_wide.hip"] + _HEADERS),
-    "bwd_dkdv": (("bwd_dkdv_kernel", "bwd_dkdv_lean_kernel"), ["attn_bwd_mfma.hip"] + _HEADERS),
+    "fwd": (("fwd_lean_kernel",), ["attn_fwd_mfma.hip"] + _HEADERS),
+    "bwd_dq": (("bwd_dq_kernel", "bwd_dq_wide_kernel"), ["attn_bwd_dq.hip", "attn_bwd_dq_wide.hip"] + _HEADERS),
+    "bwd_dkdv": (("bwd_dkdv_lean_kernel", "bwd_dkdv_wide_kernel"),
+                 ["attn_bwd_mfma.hip", "attn_bwd_dkdv_wide.hip", "kv_items.h"] + _HEADERS),
     "bwd_reduce": ("reduce_slots_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "bwd_delta": ("delta_lse2_kernel", ["attn_bwd_mfma.hip"] + _HEADERS),
     "repack": ("repack_kernel", ["repack.hip", "common.h"]),

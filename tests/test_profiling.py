@@ -22,7 +22,7 @@ def test_traffic_calibration(tmp_path):
     w = workloads.WORKLOADS["qwen3_8b"]
     copy = w.packed_len * w.n_q_heads * w.head_dim * 2
     rep = "void dualkv::(anonymous namespace)::repack_kernel<uint4>(...)"
-    dkdv = "void dualkv::(anonymous namespace)::bwd_dkdv_kernel<128>(...)"
+    dkdv = "void dualkv::(anonymous namespace)::bwd_dkdv_lean_kernel<128, 8, 3>(...)"
     # the fetch counter reads half of the copy's bytes, the write counter all of them
     _write(tmp_path / "f", "FETCH_SIZE", [(rep, copy / 2048), (dkdv, 1000.0), (dkdv, 1002.0)])
     _write(tmp_path / "w", "WRITE_SIZE", [(rep, copy / 1024), (dkdv, 10.0), (dkdv, 10.0)])
