@@ -13,10 +13,10 @@
 // Registers of a wave (32 keys, 256 head dims: all of them at head dim 256,
 // one half at 512): K^T of its keys (64 VGPRs), the 32 x 256 fp32 dK and dV
 // accumulators (256 accumulation registers), and the S and dP tiles of the
-// current stage.  At head dim 256 the item's V tile stays in LDS (row
-// operands of dP) beside a ring of two Q / dO stages; at 512 V^T of the
-// wave's half is in registers too, and the pair's partial S and dP tiles
-// meet in LDS.  This file is built without
+// current stage, and V^T of its keys (64 VGPRs; B operands of dP), so that
+// LDS holds only the ring of Q / dO stages (three at head dim 256, two at
+// 512, where the pair's partial S and dP tiles also meet in LDS).  This file
+// is built without
 // forcing MFMA results into VGPRs, so the accumulators live in the
 // accumulation registers; S and dP, for which no accumulation register is
 // left, are formed by MFMAs written as inline assembly with VGPR results
@@ -67,9 +67,6 @@ __device__ __forceinline__ void mfma_v_settle(f32x16& s, f32x16& dp) {
 template <int D, int NWK, int NS, int KDS>
 struct KvWideCfg {
   static constexpr int BK = 32 * NWK / KDS;              // keys per workgroup
-  // KDS = 1: the item's V tile in LDS, loaded once; KDS = 2: V^T in registers
-  static constexpr int V_BYTES = KDS == 1 ? BK * D * 2 : 0;
-  static constexpr int VBPW = V_BYTES / 1024 / NWK;      // its 1 KiB blocks per wave
   static constexpr int Q_BYTES = kStageRows * D * 2;     // one stage's Q rows (and dO rows)
   static constexpr int STAT_BYTES = 2 * kStageRows * 4;  // lse2 and delta of the stage's rows
   // stages start on a row boundary (a multiple of 2D bytes): a slot offset
@@ -77,13 +74,13 @@ struct KvWideCfg {
   // address untouched
   static constexpr int STAGE_BYTES = (2 * Q_BYTES + STAT_BYTES + 2 * D - 1) / (2 * D) * (2 * D);
   // KDS = 2: partial S (then dP) of every wave, 16 floats per lane
-  static constexpr int XCH_REGION = V_BYTES + NS * STAGE_BYTES;
+  static constexpr int XCH_REGION = NS * STAGE_BYTES;
   static constexpr int XCH_BYTES = KDS > 1 ? NWK * 64 * 16 * 4 : 0;
   static constexpr int LDS_BYTES = XCH_REGION + XCH_BYTES;
   static constexpr int QBLK = Q_BYTES / 1024;            // 1 KiB blocks of a Q (or dO) stage
   static constexpr int QPW = QBLK / NWK;                 // Q (and dO) blocks per wave per stage
   static_assert(QBLK % NWK == 0, "stage blocks split evenly over the waves");
-  static_assert(V_BYTES % (2 * D) == 0 && STAGE_BYTES % (2 * D) == 0, "regions on row boundaries");
+  static_assert(STAGE_BYTES % (2 * D) == 0, "stages on row boundaries");
   static_assert(Q_BYTES + 16 * 2 * D < 65536, "immediate offsets within a stage (the slot is in the base)");
 };
 
@@ -158,32 +155,28 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   const int kp_lo = posoff + it.k0;
   const int kp_hi = posoff + it.k0 + min(BK, max(klim, 1)) - 1;
 
-  // ---- this wave's 32 keys: K^T as B operands in registers; V^T too
-  // (KDS = 2) or the V tile row-major in LDS (KDS = 1, B operand of dP)
+  // ---- this wave's 32 keys: K^T and V^T as B operands in registers (of its
+  // half of the head dim when KDS = 2)
   const int wk0 = 32 * wave;
   const int my_k = wk0 + l32;
   const bool kvalid = my_k < klim;
   const int kpos = kp_lo + my_k;
   const int64_t krow = (int64_t)seg_base + it.k0 + my_k;
   const int64_t kstride = (int64_t)pr.Hkv * D;
-  bf16x8 kB[KT], vB[KDS > 1 ? KT : 1];
+  bf16x8 kB[KT], vB[KT];
 #pragma unroll
   for (int kk = 0; kk < KT; ++kk) {
     uint4 z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
     const int64_t off = krow * kstride + (int64_t)c * D + dh * DH + 16 * kk + 8 * hf;
     if (kvalid) {
       z = *reinterpret_cast<const uint4*>(k + off);
-      if constexpr (KDS > 1) y = *reinterpret_cast<const uint4*>(v + off);
+      y = *reinterpret_cast<const uint4*>(v + off);
     }
     kB[kk] = __builtin_bit_cast(bf16x8, z);
-    if constexpr (KDS > 1) vB[kk] = __builtin_bit_cast(bf16x8, y);
+    vB[kk] = __builtin_bit_cast(bf16x8, y);
   }
   wait_vmcnt<0>();                    // the loop's waits count only LDS loads
   asm volatile("" ::: "memory");
-  if constexpr (KDS == 1)
-    if (klim > 0)
-      dma_rows<D>(v + ((int64_t)seg_base + it.k0) * kstride + (int64_t)c * D, kstride, min(BK, klim), lds,
-                  wave * C::VBPW, C::VBPW, lane);
   const int wk_valid = min(32, klim - wk0);           // valid keys of this wave
   const int wkp_lo = kp_lo + wk0, wkp_hi = wkp_lo + max(wk_valid, 1) - 1;
 
@@ -210,7 +203,11 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
   StageIter s1 = s0;
   if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
-  static_assert(NS == 2, "stage ring of two: s0 in flight, s1 issued after the barrier");
+  // NS == 3: s0 and s1 in flight, s2 issued during s0's stage; NS == 2: s0
+  // in flight, s1 issued during s0's stage
+  static_assert(NS == 2 || NS == 3, "stage ring of two or three");
+  StageIter s2 = s1;
+  if (NS == 3 && s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
 
   const int64_t qstride = (int64_t)pr.Hq * D;
   const float c2 = pr.scale * kLog2e;
@@ -220,15 +217,14 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
   // operand bases (bytes from the start of LDS): Q / dO rows l32 of stage 0;
   // Q^T / dO^T transposed reads of stage 0; the stage's statistics for this
   // lane's rows
-  const unsigned vbase = row_base<D>(wk0 + l32, hf);       // V rows of this wave's keys (KDS = 1)
   // Q / dO rows: k-steps dh*KT.. of this wave's half; Q^T / dO^T: column
   // blocks dh*DB.. (the half's bits lie above those the chunk XORs address)
-  const unsigned qbase = C::V_BYTES + (row_base<D>(l32, hf) ^ ((unsigned)(dh * KT) << 5));
+  const unsigned qbase = row_base<D>(l32, hf) ^ ((unsigned)(dh * KT) << 5);
   unsigned tb0, tb1;
   trans_bases<D>(lane, tb0, tb1);
-  tb0 = C::V_BYTES + (tb0 ^ ((unsigned)(dh * DB) << 6));
-  tb1 = C::V_BYTES + (tb1 ^ ((unsigned)(dh * DB) << 6));
-  const unsigned sbase = C::V_BYTES + 2u * C::Q_BYTES + (unsigned)(4 * hf) * 4u;
+  tb0 ^= (unsigned)(dh * DB) << 6;
+  tb1 ^= (unsigned)(dh * DB) << 6;
+  const unsigned sbase = 2u * C::Q_BYTES + (unsigned)(4 * hf) * 4u;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   unsigned voff[C::QPW];
 #pragma unroll
@@ -238,7 +234,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
     const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
     const int n = min(kStageRows, st.svalid - st.r);
     const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
-    const unsigned dst = lds0 + C::V_BYTES + (unsigned)slot * C::STAGE_BYTES + (unsigned)(wave_id * C::QPW) * 1024u;
+    const unsigned dst = lds0 + (unsigned)slot * C::STAGE_BYTES + (unsigned)(wave_id * C::QPW) * 1024u;
     // Q blocks wave*QPW .. and the same dO blocks of the stage
     if (n >= kStageRows) {
 #pragma unroll
@@ -263,24 +259,34 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
       const int row = sb + st.r + min(lane & 31, n - 1);
       const float* src = (lane < 32 ? lse2 : delta) + (int64_t)st.h * pr.Tld + row;
-      const unsigned ldsaddr = lds0 + C::V_BYTES + (unsigned)slot * C::STAGE_BYTES + 2u * C::Q_BYTES;
+      const unsigned ldsaddr = lds0 + (unsigned)slot * C::STAGE_BYTES + 2u * C::Q_BYTES;
       asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(ldsaddr));
     }
   };
 
   int idx = 0;
   if (s0.ok) issue(s0, 0);
+  if (NS == 3 && s1.ok) issue(s1, 1);
   while (s0.ok) {
-    // stage s0 (and the V tile) landed: nothing else is in flight
-    wait_vmcnt<0>();
+    // stage s0 landed once only s1's loads (NS == 3) may be pending
+    if (NS == 3 && s1.ok) {
+      if (stat_wave) wait_vmcnt<2 * C::QPW + 1>();
+      else wait_vmcnt<2 * C::QPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
     block_sync();
-    if (s1.ok) issue(s1, (idx + 1) % NS);
+    // with three slots the next stage's loads go out once S and dP of this
+    // stage are formed (their LDS writes would compete with the operand
+    // reads of S and dP); with two, right away (only this stage's work is
+    // left to hide their latency)
+    if (NS == 2 && s1.ok) issue(s1, (idx + 1) % NS);
     {
       const unsigned so = (unsigned)(idx % NS) * C::STAGE_BYTES;
       // per-stage bases (the slot offset is added once; chunk XORs and
       // immediates reach every operand of the stage)
-      unsigned qb = qbase + so, t0 = tb0 + so, t1 = tb1 + so, sb4 = sbase + so, vb = vbase;
-      asm volatile("" : "+v"(qb), "+v"(t0), "+v"(t1), "+v"(sb4), "+v"(vb));
+      unsigned qb = qbase + so, t0 = tb0 + so, t1 = tb1 + so, sb4 = sbase + so;
+      asm volatile("" : "+v"(qb), "+v"(t0), "+v"(t1), "+v"(sb4));
       const int s_posoff = s0.seg < 0 ? 0 : pr.P;
       const int nrows = min(kStageRows, s0.svalid - s0.r);
       const int sq_lo = s_posoff + s0.r, sq_hi = sq_lo + nrows - 1;
@@ -301,36 +307,32 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
       if (kind != 0) {
         // S = Q K^T and dP = dO V^T into VGPRs (partial over this wave's half
-        // of the head dim when KDS = 2); the Q and dO (and V) row operands of
-        // k-step kk+2 are read before the MFMAs of step kk
+        // of the head dim when KDS = 2); the Q and dO row operands of k-step
+        // kk+2 are read before the MFMAs of step kk
         bf16x8 q0 = row_operand_x<D>(lds, qb, 0, 0), d0 = row_operand_x<D>(lds, qb, 0, C::Q_BYTES);
         bf16x8 q1 = row_operand_x<D>(lds, qb, 1, 0), d1 = row_operand_x<D>(lds, qb, 1, C::Q_BYTES);
-        bf16x8 v0 = KDS == 1 ? row_operand_x<D>(lds, vb, 0, 0) : vB[0];
-        bf16x8 v1 = KDS == 1 ? row_operand_x<D>(lds, vb, 1, 0) : vB[KDS == 1 ? 0 : 1];
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk) {
-          bf16x8 q2 = q1, d2 = d1, v2 = v1;
+          bf16x8 q2 = q1, d2 = d1;
           if (kk + 2 < KT) {
             q2 = row_operand_x<D>(lds, qb, kk + 2, 0);
             d2 = row_operand_x<D>(lds, qb, kk + 2, C::Q_BYTES);
-            if constexpr (KDS == 1) v2 = row_operand_x<D>(lds, vb, kk + 2, 0);
-            else v2 = vB[kk + 2 < KT ? kk + 2 : 0];
             __builtin_amdgcn_sched_barrier(0);
           }
           if (kk == 0) {
             s = mfma_v_first(q0, kB[0]);
-            dp = mfma_v_first(d0, v0);
+            dp = mfma_v_first(d0, vB[0]);
           } else {
             mfma_v(s, q0, kB[kk]);
-            mfma_v(dp, d0, v0);
+            mfma_v(dp, d0, vB[kk]);
           }
           __builtin_amdgcn_sched_barrier(0);
           q0 = q1; q1 = q2;
           d0 = d1; d1 = d2;
-          v0 = v1; v1 = v2;
         }
         mfma_v_settle(s, dp);
       }
+      if (NS == 3 && s2.ok) issue(s2, (idx + 2) % NS);
       if constexpr (KDS > 1) {
         // partial S, then partial dP, of this half out and the partner's in,
         // through one buffer (every wave, also on a skipped stage, so that
@@ -407,7 +409,12 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       }
     }
     s0 = s1;
-    if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
+    if (NS == 3) {
+      s1 = s2;
+      if (s2.ok) iter_next(pr, s2, kp_lo, kp_hi);
+    } else if (s1.ok) {
+      iter_next(pr, s1, kp_lo, kp_hi);
+    }
     ++idx;
   }
 
@@ -460,15 +467,15 @@ hipError_t launch_bwd_dkdv_wide(const Problem& pr, const Groups& G, const KvGrou
                                 const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                                 const float* lse2, const float* delta, uint16_t* dk, uint16_t* dv, float* part_k,
                                 float* part_v, hipStream_t stream) {
-  constexpr int NWK = 4, NS = 2;
+  constexpr int NWK = 4;
   if (pr.D == 256) {
-    static_assert(KvWideCfg<256, NWK, NS, 1>::LDS_BYTES <= 160 * 1024, "LDS budget");
-    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<256, NWK, NS, 1>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
+    static_assert(KvWideCfg<256, NWK, 3, 1>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<256, NWK, 3, 1>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
                   pr, G, kg, q, k, v, dout, lse2, delta, dk, dv, part_k, part_v);
   }
   if (pr.D == 512) {
-    static_assert(KvWideCfg<512, NWK, NS, 2>::LDS_BYTES <= 160 * 1024, "LDS budget");
-    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<512, NWK, NS, 2>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
+    static_assert(KvWideCfg<512, NWK, 2, 2>::LDS_BYTES <= 160 * 1024, "LDS budget");
+    return launch("bwd_dkdv", bwd_dkdv_wide_kernel<512, NWK, 2, 2>, dim3((unsigned)nwg), dim3(NWK * 64), 0, stream,
                   pr, G, kg, q, k, v, dout, lse2, delta, dk, dv, part_k, part_v);
   }
   return hipErrorInvalidValue;

@@ -175,8 +175,8 @@ __global__ void __launch_bounds__(NWK * 64)
   if (klim > 0) iter_fix(pr, s0, kp_lo, kp_hi);
   StageIter s1 = s0;
   if (s1.ok) iter_next(pr, s1, kp_lo, kp_hi);
-  // NS == 3: stages s0, s1 in flight, s2 issued after the barrier;
-  // NS == 2: s0 in flight, s1 issued after the barrier;
+  // NS == 3: stages s0, s1 in flight, s2 issued during s0's stage;
+  // NS == 2: s0 in flight, s1 issued during s0's stage;
   // NS == 1: s1 issued once every wave is done with the single buffer.
   static_assert(NS >= 1 && NS <= 3, "stage ring depth");
   StageIter s2 = s1;
@@ -240,11 +240,18 @@ __global__ void __launch_bounds__(NWK * 64)
       wait_vmcnt<0>();
     }
     block_sync();
-    if (NS == 3) {
-      if (s2.ok) issue(s2, (idx + 2) % NS);
-    } else if (NS == 2) {
-      if (s1.ok) issue(s1, (idx + 1) % NS);
-    }
+    // the next stage's loads go out once S, dP and dS of this stage are
+    // formed (on a skipped stage right away): issued at the barrier, their
+    // LDS writes compete with this stage's operand reads
+    bool issued = false;
+    auto issue_next = [&]() {
+      if (NS == 3) {
+        if (s2.ok) issue(s2, (idx + 2) % NS);
+      } else if (NS == 2) {
+        if (s1.ok) issue(s1, (idx + 1) % NS);
+      }
+      issued = true;
+    };
     {
       const unsigned so = (unsigned)(idx % NS) * STAGE_BYTES;
       // per-stage bases (the slot offset is added once; chunk XORs and
@@ -316,6 +323,7 @@ __global__ void __launch_bounds__(NWK * 64)
             dsB[i >> 3][i & 7] = (__bf16)ds;
           }
         }
+        issue_next();
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -328,6 +336,7 @@ __global__ void __launch_bounds__(NWK * 64)
         }
       }
     }
+    if (!issued) issue_next();
     if (NS == 1) {
       block_sync();                        // every wave is done with the buffer
       if (s1.ok) issue(s1, 0);

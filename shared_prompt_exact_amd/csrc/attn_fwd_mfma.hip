@@ -200,7 +200,6 @@ __global__ void __launch_bounds__(NW * 64)
       if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
       else wait_vmcnt<0>();
       block_sync();
-      if (it + NS - 1 < ntiles) issue(it + NS - 1);
       // opaque to the compiler: the per-chunk XORs are recomputed per tile
       // instead of being hoisted out of the loop into a dozen registers
       asm volatile("" : "+v"(kbase), "+v"(vb0), "+v"(vb1));
@@ -235,6 +234,9 @@ __global__ void __launch_bounds__(NW * 64)
           for (int kb = 0; kb < NB32; ++kb) ka[kb] = kn[kb];
         }
       }
+      // the next tile's loads go out after the score MFMAs (issued at the
+      // barrier, their LDS writes compete with the K operand reads)
+      if (it + NS - 1 < ntiles) issue(it + NS - 1);
       if constexpr (DS > 1) {
         // partial scores of this half out, the partner's in (every wave, also
         // on a skipped tile, so that the barrier is reached by all)
