@@ -8,19 +8,19 @@
 // B is stored [K][N] or, with TB, transposed as [N][K].  The three forms a
 // linear layer needs: y = x W (NN), dx = dy W^T (NT), dW = x^T dy (TN).
 //
-// Tiling: a workgroup computes a BM x 128 block of C (BM = 256 with eight
-// waves and a three-slot ring where the rows allow, else 128 with four
-// waves and two slots), each wave 64 x 64 as 2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16; K advances 64 at a time through an LDS ring
-// filled by direct global->LDS loads (the same swizzled tile layout as the
-// attention kernels).  When a k-major tile takes part (x W, x^T dy), both
-// operands number their k-slots in the order of the attention kernels'
-// transposed reads (half h of a 16-step holds k = 8*(j/4) + 4*h + j%4), so
-// k-major tiles are read transposed and an m-major tile with two 8-byte
-// reads per operand; when neither is k-major (dy W^T) both take k in
-// natural order, one 16-byte read per operand.  The wave forms C^T tiles
-// (B^T A^T), so each lane holds runs of four columns of one row of C and
-// the epilogue stores (and reads the residual) 8 bytes at a time.
+// Tiling: a workgroup computes a BM x 64*WN block of C with BM/32 waves of
+// 64 x 32*WN, as 2 x WN tiles of v_mfma_f32_32x32x16_bf16: 256 x 256 (eight
+// waves, a two-slot ring of 64-deep k tiles) where the shape allows, else
+// 256 x 128 (three slots) or 128 x 128 (four waves, two slots).  K advances
+// through an LDS ring filled by direct global->LDS loads, in the swizzled
+// tile layout of the attention kernels.  Operands: an m- or n-major tile
+// ([M][K] A, [N][K] B) is read by rows, one 16-byte read per operand, k in
+// natural order; a k-major tile is read with the transposing LDS read.  In
+// x W (only B k-major) that read takes k in natural order too; in x^T dy
+// (both k-major) both take the k-slot order of the attention kernels' C-tile
+// reuse (half h of a 16-step holds k = 8*(j/4) + 4*h + j%4).  The wave forms
+// C^T tiles (B^T A^T), so each lane holds runs of four columns of one row of
+// C and the epilogue stores (and reads the residual) 8 bytes at a time.
 //
 // Bounds: rows of an [M][K] A tile or [N][K] B tile beyond M (N) re-read
 // the last valid row and their results are not stored.  Tiles whose rows
@@ -35,6 +35,20 @@ namespace dualkv {
 namespace {
 
 constexpr int GBK = 64;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// A wave-uniform pointer in scalar registers (the scalar base of a
+// direct-to-LDS load): the compiler cannot always prove the uniformity.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const uint16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 constexpr int kWideBK = 64, kWideNS = 2;
 
 // Tile of BM x 64*WN: waves of 64 x 32*WN (WN = 2: BM = 128 with four waves,
@@ -55,19 +69,6 @@ struct GemmCfg {
   static constexpr int APW = ABLK / NW, BPW = BBLK / NW;                        // per wave
   static_assert(ABLK % NW == 0 && BBLK % NW == 0, "tile blocks split evenly over the waves");
 };
-
-// A/B operand from an m- (or n-) major tile [rows][64 k]: row `row`,
-// 16-step ks, wave half hf, k-slots in the transposed-read order.
-template <int BK>
-__device__ __forceinline__ bf16x8 kslot_row_operand(const uint16_t* tile, int row, int ks, int hf) {
-  const int c0 = 2 * ks, c1 = 2 * ks + 1;     // 16-byte chunks holding k = 16ks .. 16ks+15
-  const uint16_t* p0 = tile + row * BK + ((c0 ^ swz<BK>(row)) << 3) + 4 * hf;
-  const uint16_t* p1 = tile + row * BK + ((c1 ^ swz<BK>(row)) << 3) + 4 * hf;
-  const uint2 a = *reinterpret_cast<const uint2*>(p0);
-  const uint2 b = *reinterpret_cast<const uint2*>(p1);
-  const uint4 u = {a.x, a.y, b.x, b.y};
-  return __builtin_bit_cast(bf16x8, u);
-}
 
 template <bool TA, bool TB, int BM, int WN>
 __global__ void __launch_bounds__(BM * 2)
@@ -91,30 +92,104 @@ __global__ void __launch_bounds__(BM * 2)
   const int nk = (K + BK - 1) / BK;
 
   // operands of k tile t: its part, and the tile's first k inside the part
-  struct Ops { const uint16_t* A; int64_t lda; const uint16_t* B; int64_t ldb; int k0, Kl; };
+  struct Ops { const uint16_t* A; int64_t lda; const uint16_t* B; int64_t ldb; int k0, Kl, kp; };
   auto ops = [&](int t) {
     int kp = 0;
     if (P.ksplit)
       while (kp + 1 < P.n && t * BK >= P.lo[kp + 1]) ++kp;
     const int k_lo = P.ksplit ? P.lo[kp] : 0;
     const int bp = P.ksplit ? kp : cp;
-    return Ops{P.A[kp], P.lda[kp], P.B[bp], P.ldb[bp], t * BK - k_lo, P.ksplit ? P.lo[kp + 1] - k_lo : K};
+    return Ops{P.A[kp], P.lda[kp], P.B[bp], P.ldb[bp], t * BK - k_lo, P.ksplit ? P.lo[kp + 1] - k_lo : K, kp};
   };
 
-  // this wave's share of the 1-KiB blocks of each tile
+  // Operand addresses: one XOR-derived base per lane and operand pattern
+  // (lds_tiles.h), ring slots and the second 32-row (column) block as
+  // immediates; the wave's row (column) block is folded into the base.
+  constexpr unsigned A_BYTES = G::A_ELEMS * 2, STAGE_BYTES = G::STAGE * 2;
+  unsigned abase, a0, a1, bbase, b0, b1;
+  if constexpr (TA) {
+    trans_bases<BM>(lane, a0, a1);
+    a0 ^= (unsigned)(2 * wm) << 6;
+    a1 ^= (unsigned)(2 * wm) << 6;
+  } else {
+    abase = row_base<BK>(wm * 64 + l32, hf);
+  }
+  if constexpr (TB) {
+    bbase = A_BYTES + row_base<BK>(wn * 32 * WN + l32, hf);
+  } else {
+    if constexpr (TA) trans_bases<GBN>(lane, b0, b1);
+    else trans_bases_nat<GBN>(lane, b0, b1);
+    b0 = A_BYTES + (b0 ^ ((unsigned)(wn * WN) << 6));
+    b1 = A_BYTES + (b1 ^ ((unsigned)(wn * WN) << 6));
+  }
+
+  // Tile loads: a full tile takes a scalar base and per-lane offsets fixed
+  // for the kernel; a partial one (rows past M or N, k past K) re-reads its
+  // last valid row through dma_rows.
+  const bool a_rows_full = TA || m0 + BM <= M;
+  const bool b_rows_full = !TB || n0 + GBN <= Nl;
+  // per-lane offsets of the wave's blocks for the leading dimensions of the
+  // current part (k parts may differ; they are recomputed when it changes)
+  unsigned avoff[G::APW], bvoff[G::BPW];
+  auto lane_offsets = [&](int64_t lda, int64_t ldb) {
+#pragma unroll
+    for (int j = 0; j < G::APW; ++j)
+      avoff[j] = TA ? dma_lane_offset<BM>(wave * G::APW + j, lane, (unsigned)(lda * 2))
+                    : dma_lane_offset<BK>(wave * G::APW + j, lane, (unsigned)(lda * 2));
+#pragma unroll
+    for (int j = 0; j < G::BPW; ++j)
+      bvoff[j] = TB ? dma_lane_offset<BK>(wave * G::BPW + j, lane, (unsigned)(ldb * 2))
+                    : dma_lane_offset<GBN>(wave * G::BPW + j, lane, (unsigned)(ldb * 2));
+  };
+  int cur_kp = 0;
+  lane_offsets(P.lda[0], P.ldb[P.ksplit ? 0 : cp]);
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
   auto issue = [&](int t) {
     uint16_t* As = lds + (t % NS) * G::STAGE;
     uint16_t* Bs = As + G::A_ELEMS;
+    const unsigned adst = lds0 + (unsigned)((t % NS) * STAGE_BYTES) + (unsigned)(wave * G::APW) * 1024u;
+    const unsigned bdst = adst - (unsigned)(wave * G::APW) * 1024u + A_BYTES + (unsigned)(wave * G::BPW) * 1024u;
     const Ops o = ops(t);
+    if (o.kp != cur_kp) {                     // tiles are issued in k order: parts only advance
+      lane_offsets(o.lda, o.ldb);
+      cur_kp = o.kp;
+    }
     const int k0 = o.k0;
-    if constexpr (TA)   // [K][M]: 64 rows of k, BM m each
-      dma_rows<BM>(o.A + (int64_t)k0 * o.lda + m0, o.lda, min(BK, o.Kl - k0), As, wave * G::APW, G::APW, lane);
-    else                // [M][K]: BM rows of m, 64 k each
-      dma_rows<BK>(o.A + (int64_t)m0 * o.lda + k0, o.lda, min(BM, M - m0), As, wave * G::APW, G::APW, lane);
-    if constexpr (TB)   // [N][K]
-      dma_rows<BK>(o.B + (int64_t)n0 * o.ldb + k0, o.ldb, min(GBN, Nl - n0), Bs, wave * G::BPW, G::BPW, lane);
-    else                // [K][N]
-      dma_rows<GBN>(o.B + (int64_t)k0 * o.ldb + n0, o.ldb, min(BK, o.Kl - k0), Bs, wave * G::BPW, G::BPW, lane);
+    const bool k_full = k0 + BK <= o.Kl;
+    if constexpr (TA) {   // [K][M]: 64 rows of k, BM m each
+      const uint16_t* g = uniform_ptr(o.A + (int64_t)k0 * o.lda + m0);
+      if (k_full) {
+#pragma unroll
+        for (int j = 0; j < G::APW; ++j) dma_block(g, avoff[j], adst + j * 1024u);
+      } else {
+        dma_rows<BM>(g, o.lda, min(BK, o.Kl - k0), As, wave * G::APW, G::APW, lane);
+      }
+    } else {              // [M][K]: BM rows of m, 64 k each
+      const uint16_t* g = uniform_ptr(o.A + (int64_t)m0 * o.lda + k0);
+      if (a_rows_full) {
+#pragma unroll
+        for (int j = 0; j < G::APW; ++j) dma_block(g, avoff[j], adst + j * 1024u);
+      } else {
+        dma_rows<BK>(g, o.lda, min(BM, M - m0), As, wave * G::APW, G::APW, lane);
+      }
+    }
+    if constexpr (TB) {   // [N][K]
+      const uint16_t* g = uniform_ptr(o.B + (int64_t)n0 * o.ldb + k0);
+      if (b_rows_full) {
+#pragma unroll
+        for (int j = 0; j < G::BPW; ++j) dma_block(g, bvoff[j], bdst + j * 1024u);
+      } else {
+        dma_rows<BK>(g, o.ldb, min(GBN, Nl - n0), Bs, wave * G::BPW, G::BPW, lane);
+      }
+    } else {              // [K][N]
+      const uint16_t* g = uniform_ptr(o.B + (int64_t)k0 * o.ldb + n0);
+      if (k_full) {
+#pragma unroll
+        for (int j = 0; j < G::BPW; ++j) dma_block(g, bvoff[j], bdst + j * 1024u);
+      } else {
+        dma_rows<GBN>(g, o.ldb, min(BK, o.Kl - k0), Bs, wave * G::BPW, G::BPW, lane);
+      }
+    }
   };
 
   f32x16 acc[2][WN];
@@ -128,16 +203,20 @@ __global__ void __launch_bounds__(BM * 2)
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
     if (t < nk) issue(t);
-  for (int t = 0; t < nk; ++t) {
+  // one k tile; unrolled by the ring depth, so the slot is a compile-time
+  // constant and every operand read is a base XOR plus an immediate
+  auto step = [&](int t, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr unsigned SO = SLOT * STAGE_BYTES;
     // tile t has landed once only the later tiles' loads (up to NS-2 of
     // them, APW + BPW instructions each) are pending
     if (NS >= 3 && t + NS - 2 < nk) wait_vmcnt<(NS >= 3 ? NS - 2 : 0) * (G::APW + G::BPW)>();
     else wait_vmcnt<0>();
     block_sync();                              // everyone's; slot (t-1)%NS is free
     if (t + NS - 1 < nk) issue(t + NS - 1);
-    uint16_t* As = lds + (t % NS) * G::STAGE;
-    uint16_t* Bs = As + G::A_ELEMS;
     if constexpr (TA && !TB) {
+      uint16_t* As = lds + SLOT * G::STAGE;
+      uint16_t* Bs = As + G::A_ELEMS;
       const Ops o = ops(t);
       const int kv = o.Kl - o.k0;             // valid k rows of this tile
       if (kv < BK) {
@@ -151,21 +230,23 @@ __global__ void __launch_bounds__(BM * 2)
         block_sync();
       }
     }
+    unsigned ab = abase, x0 = a0, x1 = a1, bb = bbase, y0 = b0, y1 = b1;
+    if constexpr (TA) asm volatile("" : "+v"(x0), "+v"(x1));
+    else asm volatile("" : "+v"(ab));
+    if constexpr (TB) asm volatile("" : "+v"(bb));
+    else asm volatile("" : "+v"(y0), "+v"(y1));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 a[2], b[WN];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int mr = wm * 64 + i * 32;
-        if constexpr (TA) a[i] = trans_operand<BM>(As, 0, mr, ks, lane);
-        else if constexpr (TB) a[i] = row_operand<BK>(As, mr + l32, ks, hf);
-        else a[i] = kslot_row_operand<BK>(As, mr + l32, ks, hf);
+        if constexpr (TA) a[i] = trans_operand_x<BM>(lds, x0, x1, i, ks, SO);
+        else a[i] = row_operand_x<BK>(lds, ab, ks, SO + (unsigned)(i * 32 * BK * 2));
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        const int nr = wn * 32 * WN + j * 32;
-        if constexpr (TB) b[j] = row_operand<BK>(Bs, nr + l32, ks, hf);
-        else b[j] = trans_operand<GBN>(Bs, 0, nr, ks, lane);
+        if constexpr (TB) b[j] = row_operand_x<BK>(lds, bb, ks, SO + (unsigned)(j * 32 * BK * 2));
+        else b[j] = trans_operand_x<GBN>(lds, y0, y1, j, ks, SO);   // natural k order unless TA
       }
       // the product is formed transposed (C^T tile = B^T A^T), so that a
       // lane holds four consecutive columns of C in each register group
@@ -174,7 +255,17 @@ __global__ void __launch_bounds__(BM * 2)
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
     }
+  };
+  static_assert(NS == 2 || NS == 3, "ring of two or three, unrolled by its depth");
+  int t = 0;
+  for (; t + NS <= nk; t += NS) {
+    step(t, IntC<0>{});
+    step(t + 1, IntC<1>{});
+    if constexpr (NS == 3) step(t + 2, IntC<2 % NS>{});
   }
+  if (t < nk) step(t, IntC<0>{});
+  if constexpr (NS == 3)
+    if (t + 1 < nk) step(t + 1, IntC<1>{});
 
   // C^T tile (i, j): lane row m, columns 8*(e/4) + 4*hf + e%4; four
   // consecutive columns go out (and the residual comes in) as 8 bytes
@@ -259,8 +350,10 @@ int gemm_shape_ok(bool ta, bool tb, int M, int N, int K, int64_t lda, int64_t ld
   if (ta && M % 128 != 0) return 0;            // k-major A: whole 128-wide m blocks
   if (!tb && N % GBN != 0) return 0;           // k-major B: whole 128-wide n blocks
   if (!(ta && !tb) && K % GBK != 0) return 0;  // k along tile columns: whole 64-wide k blocks
-  // 16-byte global rows for the direct-to-LDS loads
+  // 16-byte global rows for the direct-to-LDS loads, whose per-lane byte
+  // offsets inside a tile (up to 256 rows) are 32-bit
   if (lda % 8 != 0 || ldb % 8 != 0) return 0;
+  if (lda >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 22)) return 0;
   if ((int64_t)((M + 127) / 128) * ((N + GBN - 1) / GBN) >= ((int64_t)1 << 31)) return 0;
   return 1;
 }

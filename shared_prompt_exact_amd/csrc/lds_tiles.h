@@ -118,6 +118,27 @@ __device__ __forceinline__ bf16x8 trans_operand(const uint16_t* tile, int row0, 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// The same transposed operand with k in natural order (slot j of half h <->
+// row 8*h + j), for a product whose other operand is a plain row read: the
+// two reads take rows 8h .. 8h+3 and 8h+4 .. 8h+7 of the step.  Each group of
+// 16 lanes still reads four consecutive rows (four values of swz bits 2-3)
+// by four consecutive chunks, so it stays free of bank conflicts.
+template <int D>
+__device__ __forceinline__ bf16x8 trans_operand_nat(const uint16_t* tile, int row0, int col0, int ks,
+                                                    int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int hf = g >> 1, ib = (g & 1) * 16;
+  const int col = col0 + ib + 4 * (s & 3);
+  const int r0 = row0 + 16 * ks + 8 * hf + (s >> 2);
+  const lds_short4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_as3*)(tile + tile_off<D>(r0, col)));
+  const lds_short4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4_as3*)(tile + tile_off<D>(r0 + 4, col)));
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  const uint4 u = {x.x, x.y, y.x, y.y};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // ---- XOR-addressed operand reads -------------------------------------------
 //
 // In a swizzled tile the byte address of (row, chunk c) is
@@ -156,6 +177,18 @@ __device__ __forceinline__ void trans_bases(int lane, unsigned& b0, unsigned& b1
   const int r0 = 4 * hf + (s >> 2);                  // 0 .. 7
   b0 = (unsigned)r0 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r0))) << 4) + (unsigned)((col & 7) * 2);
   const int r1 = r0 + 8;
+  b1 = (unsigned)r1 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r1))) << 4) + (unsigned)((col & 7) * 2);
+}
+
+// Bases of the natural-order transposed operand (see trans_operand_nat).
+template <int D>
+__device__ __forceinline__ void trans_bases_nat(int lane, unsigned& b0, unsigned& b1) {
+  const int g = lane >> 4, s = lane & 15;
+  const int hf = g >> 1, ib = (g & 1) * 16;
+  const int col = ib + 4 * (s & 3);                  // 0 .. 31
+  const int r0 = 8 * hf + (s >> 2);                  // 0 .. 11
+  b0 = (unsigned)r0 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r0))) << 4) + (unsigned)((col & 7) * 2);
+  const int r1 = r0 + 4;
   b1 = (unsigned)r1 * (2 * D) + (unsigned)((((col >> 3) ^ swz<D>(r1))) << 4) + (unsigned)((col & 7) * 2);
 }
 
