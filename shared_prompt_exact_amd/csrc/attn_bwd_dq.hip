@@ -149,13 +149,30 @@ __global__ void __launch_bounds__(NW * 64)
     const TileRange tr = key_tiles(pr, b, b.r0, blk_hi, BN);
     const int ntiles = tr.nA + tr.nB;
     const int64_t rs = (int64_t)pr.Hkv * D;
+    // full tiles load from a scalar base plus per-lane offsets fixed for the
+    // kernel; a partial tile re-reads its last valid row through dma_rows
+    unsigned voff[C::BPW];
+#pragma unroll
+    for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::BPW + j, lane, (unsigned)(rs * 2));
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     auto issue = [&](int t) {
       const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
       uint16_t* slot = lds + (t % NS) * C::STAGE;
       const int nv = min(BN, kt.lim);
-      dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
-      dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
+      if (nv >= BN) {
+        const uint16_t* kg = uniform_ptr(k + off);
+        const uint16_t* vg = uniform_ptr(v + off);
+        const unsigned dst = lds0 + (unsigned)((t % NS) * C::STAGE * 2) + (unsigned)(wave * C::BPW) * 1024u;
+#pragma unroll
+        for (int j = 0; j < C::BPW; ++j) {
+          dma_block(kg, voff[j], dst + j * 1024u);
+          dma_block(vg, voff[j], dst + C::K_ELEMS * 2 + j * 1024u);
+        }
+      } else {
+        dma_rows<D>(k + off, rs, nv, slot, wave * C::BPW, C::BPW, lane);
+        dma_rows<D>(v + off, rs, nv, slot + C::K_ELEMS, wave * C::BPW, C::BPW, lane);
+      }
     };
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)

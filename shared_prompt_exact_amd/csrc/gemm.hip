@@ -41,14 +41,6 @@ struct IntC {
   static constexpr int value = V;
 };
 
-// A wave-uniform pointer in scalar registers (the scalar base of a
-// direct-to-LDS load): the compiler cannot always prove the uniformity.
-__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
-  const uint64_t u = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const uint16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
 constexpr int kWideBK = 64, kWideNS = 2;
 
 // Tile of BM x 64*WN: waves of 64 x 32*WN (WN = 2: BM = 128 with four waves,

@@ -221,6 +221,20 @@ __device__ __forceinline__ unsigned dma_lane_offset(int blk, int lane, unsigned 
   return (unsigned)row * row_bytes + (unsigned)c * 16u;
 }
 
+// A wave-uniform pointer in scalar registers (the scalar base of a
+// direct-to-LDS load) when the compiler cannot prove the uniformity.  Both
+// halves go through unsigned 32-bit values: readfirstlane returns int, and a
+// sign-extended low half would set the upper 32 bits.
+__device__ __forceinline__ uint64_t join_halves(uint32_t lo, uint32_t hi) {
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (const uint16_t*)(uintptr_t)join_halves(lo, hi);
+}
+
 // One 1 KiB block of a tile by direct global->LDS load: global address
 // `gbase` (wave-uniform, scalar) + this lane's offset, LDS destination
 // `lds_byte` (wave-uniform).  No vector arithmetic on the address.
