@@ -175,6 +175,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
     const int64_t rs = (int64_t)pr.Hkv * D;
     const unsigned row_bytes = (unsigned)(rs * 2);
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    // per-lane offsets of the wave's blocks in a full tile, fixed for the kernel
+    unsigned voff[C::BPW];
+#pragma unroll
+    for (int j = 0; j < C::BPW; ++j) voff[j] = dma_lane_offset<D>(wave * C::BPW + j, lane, row_bytes);
     auto issue = [&](int t) {
       const KeyTile kt = tile_at(pr, b, tr, t, BN);
       const int64_t off = (int64_t)kt.row0 * rs + (int64_t)c * D;
@@ -182,6 +186,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
       const unsigned vdst = kdst + C::V_REGION;
       const uint16_t* kg = k + off;
       const uint16_t* vg = v + off;
+      if (kt.lim >= BN) {
+#pragma unroll
+        for (int j = 0; j < C::BPW; ++j) {
+          dma_block(kg, voff[j], kdst + j * 1024);
+          dma_block(vg, voff[j], vdst + j * 1024);
+        }
+        return;
+      }
       constexpr int CPR = D / 8, RPB = 64 / CPR;
       int ln = lane;
       asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
