@@ -5,7 +5,7 @@
 // "DualKV: Shared-Prompt Flash Attention ..." (arXiv 2605.15422), Abstract:
 // the gradient of a shared-prompt key or value sums the contributions of
 // the prompt's own queries and of every response.  Work items, stages,
-// masks, slot partials and the arithmetic are those of bwd_dkdv_kernel
+// masks, slot partials and the arithmetic are those of bwd_dkdv_lean_kernel
 // (attn_bwd_mfma.hip): per visible (query i, key j) pair p = exp(scale q.k -
 // LSE_i), dp = dO_i . v_j, ds = p (dp - Delta_i), dV_j += p dO_i,
 // dK_j += scale ds q_i.
