@@ -312,7 +312,7 @@ template hipError_t launch_bwd_dq<64, 64, 8, 3>(const Problem&, const Groups&, c
                                                    const uint16_t*, const uint16_t*, const uint16_t*,
                                                    const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                    uint16_t*, hipStream_t);
-template hipError_t launch_bwd_dq<128, 32, 8, 3>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
+template hipError_t launch_bwd_dq<128, 32, 4, 3>(const Problem&, const Groups&, const GroupBlocks&, int, int64_t,
                                                     const uint16_t*, const uint16_t*, const uint16_t*,
                                                     const uint16_t*, const uint16_t*, const float*, float*, float*,
                                                     uint16_t*, hipStream_t);

@@ -71,7 +71,8 @@ __global__ void __launch_bounds__(NWK * 64)
   constexpr int KT = D / 16, DB = D / 32, BK = C::BK;
   constexpr unsigned V_BYTES = C::V_ELEMS * 2, Q_BYTES = C::Q_ELEMS * 2, DO_BYTES = C::DO_ELEMS * 2;
   constexpr unsigned STAGE_BYTES = C::STAGE * 2;
-  static_assert(C::SBPW == 2 && C::QBLK == NWK, "one Q block and one dO block per wave and stage");
+  static_assert(C::QBLK % NWK == 0, "whole Q and dO blocks per wave and stage");
+  constexpr int QPW = C::QBLK / NWK;
   static_assert(V_BYTES % (2 * D) == 0 && STAGE_BYTES % (2 * D) == 0,
                 "slot offsets added to operand bases leave the XOR-addressed bits alone");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_BYTES / 2];
@@ -198,26 +199,34 @@ __global__ void __launch_bounds__(NWK * 64)
   tb1 += V_BYTES;
   unsigned sbase = V_BYTES + Q_BYTES + DO_BYTES + (unsigned)(4 * hf) * 4u;
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-  const unsigned voff = dma_lane_offset<D>(wave, lane, (unsigned)(qstride * 2));
+  unsigned voff[QPW];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) voff[j] = dma_lane_offset<D>(wave * QPW + j, lane, (unsigned)(qstride * 2));
 
   auto issue = [&](const StageIter& st, int slot) {
     const int sb = st.seg < 0 ? 0 : pr.P + st.seg * pr.R;
     const int n = min(kStageRows, st.svalid - st.r);
     const int64_t off = ((int64_t)sb + st.r) * qstride + (int64_t)st.h * D;
-    const unsigned dst = lds0 + V_BYTES + (unsigned)slot * STAGE_BYTES + (unsigned)wave * 1024u;
-    // Q block `wave` and dO block `wave` of the stage
+    const unsigned dst = lds0 + V_BYTES + (unsigned)slot * STAGE_BYTES + (unsigned)(wave * QPW) * 1024u;
+    // Q blocks wave*QPW.. and the same dO blocks of the stage
     if (n >= kStageRows) {
-      dma_block(q + off, voff, dst);
-      dma_block(dout + off, voff, dst + Q_BYTES);
+#pragma unroll
+      for (int j = 0; j < QPW; ++j) {
+        dma_block(q + off, voff[j], dst + j * 1024u);
+        dma_block(dout + off, voff[j], dst + Q_BYTES + j * 1024u);
+      }
     } else {
       constexpr int CPR = D / 8, RPB = 64 / CPR;
       int ln = lane;
       asm volatile("" : "+v"(ln));      // computed here, not kept live across the loop
-      const int row = wave * RPB + ln / CPR;
-      const int src = min(row, n - 1);
-      const unsigned vo = (unsigned)src * (unsigned)(qstride * 2) + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
-      dma_block(q + off, vo, dst);
-      dma_block(dout + off, vo, dst + Q_BYTES);
+#pragma unroll
+      for (int j = 0; j < QPW; ++j) {
+        const int row = (wave * QPW + j) * RPB + ln / CPR;
+        const int src = min(row, n - 1);
+        const unsigned vo = (unsigned)src * (unsigned)(qstride * 2) + (unsigned)(((ln % CPR) ^ swz<D>(row)) * 16);
+        dma_block(q + off, vo, dst + j * 1024u);
+        dma_block(dout + off, vo, dst + Q_BYTES + j * 1024u);
+      }
     }
     if (stat_wave) {
       // 64 lanes x 4 bytes: lse2 of the 32 rows, then their delta
@@ -476,10 +485,13 @@ __global__ void __launch_bounds__(256)
 // waves per SIMD; at 256 and 512 one, with the accumulators in the
 // accumulation registers (attn_bwd_dq_wide.hip, attn_bwd_dkdv_wide.hip), and
 // at 512 a wave pair splits the head dim, so that a wave holds at most 256
-// dims of its operands and accumulators.  The dK/dV kernel at head dim 64
-// runs four waves (one 32-row Q and dO block per wave and stage).
-inline int dq_waves(int D) { return D >= 256 ? 4 : 8; }
-inline int kv_waves(int D) { return D == 128 ? 8 : 4; }
+// dims of its operands and accumulators.  The dK/dV kernel runs four waves
+// at every head dim: at 128 (a 128-key item, V tile and a two-stage ring in
+// 66 KB of LDS) two workgroups share a CU, so that the barriers of one do
+// not hold the waves of the other (8.9 against 9.35 ms for eight waves and
+// 256-key items on the Qwen3-8B shape).
+inline int dq_waves(int D) { return D >= 128 ? 4 : 8; }
+inline int kv_waves(int) { return 4; }
 inline int dq_split(int D) { return D <= 256 ? 1 : 2; }
 inline int kv_split(int D) { return D <= 256 ? 1 : 2; }
 
@@ -689,7 +701,7 @@ hipError_t launch_bwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   switch (pr.D) {
     //                D  NW NWK BN DQNS KVNS DS
     case 64: return run<64, 8, 4, 64, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
-    case 128: return run<128, 8, 8, 32, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
+    case 128: return run<128, 4, 4, 32, 3, 2, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 256: return run<256, 4, 4, 32, 3, 3, 1>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     case 512: return run<512, 4, 4, 32, 2, 2, 2>(pr, G, p, q, k, v, o, lse, dout, dq, dk, dv, ws, stream);
     default: return hipErrorInvalidValue;
