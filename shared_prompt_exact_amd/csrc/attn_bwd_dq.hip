@@ -17,15 +17,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A compile-time ring slot: the tile loop is unrolled by the ring depth.
 template <int V>
 struct IntC {
   static constexpr int value = V;
 };
-// Ring slot of a tile: a compile-time constant (IntC) on the unrolled path,
-// a runtime value otherwise.
-template <int V>
-__device__ __forceinline__ constexpr int slot_value(IntC<V>) { return V; }
-__device__ __forceinline__ int slot_value(int x) { return x; }
 
 // ----------------------------------------------------------------- dq kernel
 
@@ -181,7 +177,7 @@ __global__ void __launch_bounds__(NW * 64)
     // a compile-time constant, so LDS addresses are per-lane bases plus
     // immediates.
     auto step = [&](int it, auto slot_c) {
-      const int SLOT = slot_value(slot_c);
+      constexpr int SLOT = decltype(slot_c)::value;
       if (it + 1 < ntiles) wait_vmcnt<2 * C::BPW * (NS - 2)>();
       else wait_vmcnt<0>();
       block_sync();
