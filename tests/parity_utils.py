@@ -13,8 +13,14 @@ REL_L2 = {"f32": 1e-5, "bf16": 1e-2}
 MAX_ERR_BF16 = 2e-2
 # On inputs that are not unit variance (the 0.5-scaled layer shapes) the
 # elementwise gate is a detector of localised faults (a wrong row or tile
-# gives errors of order |y|): |x - y| <= 0.1 * max(RMS(y), |y|).
+# gives errors of order |y|): |x - y| <= f * max(RMS(y), |y|), f = 0.04 for O,
+# dK and dV and 0.1 for dQ.  On the five full-size configs the kernels reach
+# at most 0.016 (O, dK, dV) and 0.068 (dQ, where the bf16 rounding of O
+# inside Delta moves single elements most); the results are bitwise
+# reproducible, so these do not vary from run to run.
 LOCAL_FAULT = 0.1
+LOCAL_FAULT_BY_NAME = {"o": 0.04, "dk": 0.04, "dv": 0.04, "dq": 0.1}
+LAST_LOCAL = [float("nan")]   # the last |x-y|/max(RMS,|y|) of that gate, for the logs
 
 
 def to_dev(a, dtype):
@@ -46,6 +52,7 @@ def check(name, got, ref, dtype, unit_variance=True, elementwise=True, envelope=
         assert np.array_equal(inf_ref, inf_got), f"{name}: -inf positions differ"
         got, ref = got[~inf_ref], ref[~inf_ref]
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    LAST_LOCAL[0] = float("nan")
     err = rel_l2(got, ref)
     mab = float(np.abs(got - ref).max()) if got.size else 0.0
     assert err <= REL_L2[dtype], f"{name}: rel-L2 {err:.3e} > {REL_L2[dtype]}"
@@ -61,7 +68,9 @@ def check(name, got, ref, dtype, unit_variance=True, elementwise=True, envelope=
         else:
             rms = float(np.sqrt(np.mean(ref ** 2)))
             worst = float((diff / np.maximum(rms, np.abs(ref))).max())
-            assert worst <= LOCAL_FAULT, f"{name}: |x-y|/max(RMS,|y|) = {worst:.3e} > {LOCAL_FAULT}"
+            LAST_LOCAL[0] = worst
+            bound = LOCAL_FAULT_BY_NAME.get(name, LOCAL_FAULT)
+            assert worst <= bound, f"{name}: |x-y|/max(RMS,|y|) = {worst:.3e} > {bound}"
     return err, mab
 
 
