@@ -126,7 +126,7 @@ def test_full_size_layer(name):
     ref = orows.query_rows(x.q, x.k, x.v, x.do, qr, N, P, R, w.window, None, x.valid_len)
     for nm, got, want in (("o", O[qr], ref["o"]), ("lse", LSE[:, qr], ref["lse"]),
                           ("dq", DQ[qr], ref["dq"])):
-        log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False) + " local %.2e" % parity_utils.LAST_LOCAL[0])
+        log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False, local_fault=parity_utils.FULL_SIZE_LOCAL_FAULT.get(nm, parity_utils.LOCAL_FAULT)) + " local %.2e" % parity_utils.LAST_LOCAL[0])
 
     # sampled response key rows, first and last KV head
     kr = sorted(set(sample_key_rows(w, L, 0) + sample_key_rows(w, L, N - 1)))
@@ -134,7 +134,7 @@ def test_full_size_layer(name):
         log(f"{name}: oracle on response key rows {kr}, KV head {c}")
         ref = orows.key_rows(x.q, x.k, x.v, x.do, kr, c, N, P, R, w.window, None, x.valid_len)
         for nm, got, want in (("dk", DK[kr, c], ref["dk"]), ("dv", DV[kr, c], ref["dv"])):
-            log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False) + " local %.2e" % parity_utils.LAST_LOCAL[0])
+            log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False, local_fault=parity_utils.FULL_SIZE_LOCAL_FAULT.get(nm, parity_utils.LOCAL_FAULT)) + " local %.2e" % parity_utils.LAST_LOCAL[0])
 
     # sampled prompt key rows: the sum over the prompt's queries and all N
     # responses
@@ -147,7 +147,7 @@ def test_full_size_layer(name):
             log(f"{name}: oracle on prompt key rows {pk}, KV head {c}, all {g} query heads ({cost * g:.2e} scores)")
             ref = orows.key_rows(x.q, x.k, x.v, x.do, pk, c, N, P, R, w.window, None, x.valid_len)
             for nm, got, want in (("dk", DK[pk, c], ref["dk"]), ("dv", DV[pk, c], ref["dv"])):
-                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False) + " local %.2e" % parity_utils.LAST_LOCAL[0])
+                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False, local_fault=parity_utils.FULL_SIZE_LOCAL_FAULT.get(nm, parity_utils.LOCAL_FAULT)) + " local %.2e" % parity_utils.LAST_LOCAL[0])
         else:
             h1 = w.n_q_heads - 1
             c = h1 // g
@@ -168,7 +168,7 @@ def test_full_size_layer(name):
             ref = orows.key_rows(x.q, x.k, x.v, xdo, pk, c, N, P, R, w.window, None, x.valid_len)
             del xdo
             for nm, got, want in (("dk", DK1, ref["dk"]), ("dv", DV1, ref["dv"])):
-                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False) + " local %.2e" % parity_utils.LAST_LOCAL[0])
+                log(f"  {nm}: rel-L2 %.2e max-abs %.2e" % check(nm, got, want, w.dtype, False, local_fault=parity_utils.FULL_SIZE_LOCAL_FAULT.get(nm, parity_utils.LOCAL_FAULT)) + " local %.2e" % parity_utils.LAST_LOCAL[0])
     del d, o, lse
     torch.cuda.empty_cache()
 
