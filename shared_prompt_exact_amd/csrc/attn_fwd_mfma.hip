@@ -365,10 +365,12 @@ FwdPlan plan(const Problem& pr, const Groups& G) {
   FwdPlan p;
   // Per wave, Q^T and the O accumulator take 3*D/4 registers.  With the
   // XOR-derived operand addresses a wave holds D = 256 whole at two waves
-  // per SIMD (242 registers; 32-key tiles) and D = 128 at three (twelve
-  // waves, 164 registers); D = 512 splits the head dim over wave pairs
-  // (247 registers, two waves per SIMD).
-  p.NW = pr.D == 128 ? 12 : 8;
+  // per SIMD (243 registers; 32-key tiles, four-wave workgroups with a
+  // two-slot ring, two per CU, so that one workgroup's barriers do not hold
+  // the other's waves) and D = 128 at three (twelve waves, 168 registers);
+  // D = 512 splits the head dim over wave pairs (248 registers, two waves
+  // per SIMD).
+  p.NW = pr.D == 128 ? 12 : pr.D == 256 ? 4 : 8;
   p.BN = pr.D <= 128 ? 64 : 32;
   p.DS = pr.D <= 256 ? 1 : 2;
   p.HG = 1;   // query heads per block: a power of two dividing g and the waves' row slots
@@ -415,7 +417,7 @@ hipError_t launch_fwd_mfma(const Problem& pr, const Groups& G, const void* q, co
   switch (pr.D) {
     case 64: return run_lean<64, 64, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
     case 128: return run_lean<128, 64, 12, 3>(pr, G, p, q, k, v, o, lse, stream);
-    case 256: return run_lean<256, 32, 8, 3>(pr, G, p, q, k, v, o, lse, stream);
+    case 256: return run_lean<256, 32, 4, 2>(pr, G, p, q, k, v, o, lse, stream);
     case 512: return run_lean<512, 32, 8, 2, 2>(pr, G, p, q, k, v, o, lse, stream);   // 64 KiB per slot
     default: return hipErrorInvalidValue;
   }
