@@ -281,25 +281,19 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
         {
-          // S = Q K^T and dP = dO V^T; the operand reads of k-step kk+1 are
-          // issued before the two MFMAs of step kk (scheduling fences)
-          bf16x8 qa = row_operand_x<D>(lds, qb, 0, 0), da = row_operand_x<D>(lds, qb, 0, Q_BYTES);
-          bf16x8 vv = row_operand_x<D>(lds, vb, 0, 0);
+          // S = Q K^T as one chain (Q operands read one k-step ahead,
+          // scheduling fences keep each read before the MFMA it feeds)
+          bf16x8 qa = row_operand_x<D>(lds, qb, 0, 0);
 #pragma unroll
           for (int kk = 0; kk < KT; ++kk) {
-            bf16x8 qn = qa, dn = da, vn = vv;
+            bf16x8 qn = qa;
             if (kk + 1 < KT) {
               qn = row_operand_x<D>(lds, qb, kk + 1, 0);
-              dn = row_operand_x<D>(lds, qb, kk + 1, Q_BYTES);
-              vn = row_operand_x<D>(lds, vb, kk + 1, 0);
               __builtin_amdgcn_sched_barrier(0);
             }
             s = mfma32(qa, kB[kk], s);
-            dp = mfma32(da, vv, dp);
             __builtin_amdgcn_sched_barrier(0);
             qa = qn;
-            da = dn;
-            vv = vn;
           }
         }
         if (kind == 2) {
@@ -316,19 +310,49 @@ __global__ void __launch_bounds__(NWK * 64)
             s[i] = vis ? s[i] : -INFINITY;
           }
         }
+        {
+          // dP = dO V^T as a second chain; beside each of its MFMAs the
+          // wave turns 16/KT scores into p = exp2(s c - lse2) (S is complete,
+          // so this vector work overlaps the wave's own matrix work)
+          constexpr int EPM = 16 / KT;
+          static_assert(EPM * KT == 16 && EPM <= 4, "whole score elements per dP MFMA");
+          bf16x8 da = row_operand_x<D>(lds, qb, 0, Q_BYTES), vv = row_operand_x<D>(lds, vb, 0, 0);
+          float4 l4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4));   // lse2 of rows 0-3 (+4*hf)
+#pragma unroll
+          for (int kk = 0; kk < KT; ++kk) {
+            bf16x8 dn = da, vn = vv;
+            float4 ln = l4;
+            if (kk + 1 < KT) {
+              dn = row_operand_x<D>(lds, qb, kk + 1, Q_BYTES);
+              vn = row_operand_x<D>(lds, vb, kk + 1, 0);
+              const int gn = (EPM * (kk + 1)) >> 2;           // row group of the next elements
+              if (gn != (EPM * kk) >> 2) ln = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * gn));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dp = mfma32(da, vv, dp);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < EPM; ++e) {
+              const int i = EPM * kk + e;                      // register index
+              s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[i & 3]));
+              asm volatile("" : "+v"(s[i]));                   // formed here, beside the MFMA
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            da = dn;
+            vv = vn;
+            l4 = ln;
+          }
+        }
         bf16x8 pB[2], dsB[2];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * g4));
           const float4 d4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * g4 + kStageRows * 4));
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;                       // register index
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e]));
-            const float ds = p * (dp[i] - dv4[e]);
-            pB[i >> 3][i & 7] = (__bf16)p;
+            const int i = 4 * g4 + e;
+            const float ds = s[i] * (dp[i] - dv4[e]);
+            pB[i >> 3][i & 7] = (__bf16)s[i];
             dsB[i >> 3][i & 7] = (__bf16)ds;
           }
         }
