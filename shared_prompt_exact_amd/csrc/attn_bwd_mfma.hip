@@ -345,26 +345,55 @@ __global__ void __launch_bounds__(NWK * 64)
         }
         bf16x8 pB[2], dsB[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 d4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * g4 + kStageRows * 4));
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int i = 0; i < 16; ++i) pB[i >> 3][i & 7] = (__bf16)s[i];
+        issue_next();
+        {
+          // dV += dO^T P (transposed operands one MFMA ahead); beside each
+          // MFMA the wave forms dS = P (dP - Delta) of two elements
+          constexpr int EPD = 8 / DB;                 // dS elements per dV MFMA
+          static_assert(EPD * 2 * DB == 16 && EPD <= 4, "whole dS elements per dV MFMA");
+          float4 d4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + kStageRows * 4));   // Delta, rows 0-3
+          bf16x8 cur = trans_operand_x<D>(lds, t0, t1, 0, 0, Q_BYTES);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;
-            const float ds = s[i] * (dp[i] - dv4[e]);
-            pB[i >> 3][i & 7] = (__bf16)s[i];
-            dsB[i >> 3][i & 7] = (__bf16)ds;
+          for (int m = 0; m < 2 * DB; ++m) {
+            const int db = m >> 1, ks = m & 1;
+            bf16x8 nxt = cur;
+            float4 dn = d4;
+            if (m + 1 < 2 * DB) {
+              nxt = trans_operand_x<D>(lds, t0, t1, (m + 1) >> 1, (m + 1) & 1, Q_BYTES);
+              const int gn = (EPD * (m + 1)) >> 2;      // row group of the next elements
+              if (gn != (EPD * m) >> 2)
+                dn = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * gn + kStageRows * 4));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dVt[db] = mfma32(cur, pB[ks], dVt[db]);
+            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < EPD; ++e) {
+              const int i = EPD * m + e;
+              float x = s[i] * (dp[i] - dv4[i & 3]);
+              asm volatile("" : "+v"(x));              // formed here, beside the MFMA
+              dsB[i >> 3][i & 7] = (__bf16)x;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+            d4 = dn;
           }
         }
-        issue_next();
+        {
+          // dK += Q^T dS (transposed operands one MFMA ahead)
+          bf16x8 cur = trans_operand_x<D>(lds, t0, t1, 0, 0, 0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 da = trans_operand_x<D>(lds, t0, t1, db, ks, Q_BYTES);
-            const bf16x8 qa = trans_operand_x<D>(lds, t0, t1, db, ks, 0);
-            dVt[db] = mfma32(da, pB[ks], dVt[db]);
-            dKt[db] = mfma32(qa, dsB[ks], dKt[db]);
+          for (int m = 0; m < 2 * DB; ++m) {
+            const int db = m >> 1, ks = m & 1;
+            bf16x8 nxt = cur;
+            if (m + 1 < 2 * DB) {
+              nxt = trans_operand_x<D>(lds, t0, t1, (m + 1) >> 1, (m + 1) & 1, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dKt[db] = mfma32(cur, dsB[ks], dKt[db]);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
           }
         }
       }
