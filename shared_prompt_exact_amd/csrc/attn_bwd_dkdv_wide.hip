@@ -63,6 +63,9 @@ __device__ __forceinline__ float acc_read(float a) {
 __device__ __forceinline__ void mfma_v_settle(f32x16& s, f32x16& dp) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s), "+v"(dp));
 }
+__device__ __forceinline__ void mfma_v_settle1(f32x16& t) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(t));
+}
 
 template <int D, int NWK, int NS, int KDS>
 struct KvWideCfg {
@@ -296,6 +299,121 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
       else if (wk_valid == 32 && nrows == kStageRows && sq_lo >= wkp_hi &&
                (pr.W <= 0 || sq_hi - wkp_lo < pr.W)) kind = 1;
       else kind = 2;
+      if constexpr (KDS == 1) {
+        // S and dP as two chains: beside each dP MFMA the wave turns one
+        // score into p = exp2(s c - lse2); then the dV products with dS =
+        // p (dp - Delta) of one element formed beside each, then the dK
+        // products.  One wave per SIMD: only the wave's own vector work can
+        // overlap its matrix work.  On a skipped stage P and dS stay zero
+        // and the dV / dK products still run (the accumulators are updated
+        // on one path only).
+        static_assert(KT == 16 && DB == 8, "one score element per dP and per dV MFMA");
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        if (kind != 0) {
+          bf16x8 q0 = row_operand_x<D>(lds, qb, 0, 0), q1 = row_operand_x<D>(lds, qb, 1, 0);
+#pragma unroll
+          for (int kk = 0; kk < KT; ++kk) {
+            bf16x8 q2 = q1;
+            if (kk + 2 < KT) {
+              q2 = row_operand_x<D>(lds, qb, kk + 2, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kk == 0) s = mfma_v_first(q0, kB[0]);
+            else mfma_v(s, q0, kB[kk]);
+            __builtin_amdgcn_sched_barrier(0);
+            q0 = q1; q1 = q2;
+          }
+        }
+        if (NS == 3 && s2.ok) issue(s2, (idx + 2) % NS);
+        if (kind != 0) {
+          bf16x8 d0 = row_operand_x<D>(lds, qb, 0, C::Q_BYTES), d1 = row_operand_x<D>(lds, qb, 1, C::Q_BYTES);
+          float4 l4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4));   // lse2 of rows 0-3 (+4*hf)
+#pragma unroll
+          for (int kk = 0; kk < KT; ++kk) {
+            bf16x8 d2 = d1;
+            float4 ln = l4;
+            if (kk + 2 < KT) {
+              d2 = row_operand_x<D>(lds, qb, kk + 2, C::Q_BYTES);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kk == 0) {
+              dp = mfma_v_first(d0, vB[0]);
+              mfma_v_settle1(s);                        // S is read from here on
+              if (kind == 2) {
+                // query qc (+4*hf) of the stage is visible to this lane's key
+                // iff 0 <= qpos - kpos < window and qc < nrows (branch-free);
+                // hidden scores become -inf, so p = exp2(-inf - lse2) = 0.
+                int e0 = sq_lo + 4 * hf - kpos;
+                int n0 = (kvalid ? nrows : 0) - 4 * hf;
+                asm volatile("" : "+v"(e0), "+v"(n0));   // no per-element constants hoisted
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int qc = 8 * (i >> 2) + (i & 3);     // query row - 4*hf
+                  const bool vis = ((unsigned)(e0 + qc) < wspan) & (qc < n0);
+                  s[i] = vis ? s[i] : -INFINITY;
+                }
+              }
+            } else {
+              mfma_v(dp, d0, vB[kk]);
+              const int i = kk - 1;                      // element of this MFMA
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[i & 3]));
+              asm volatile("" : "+v"(s[i]));             // formed here, beside the MFMA
+              if ((i & 3) == 3) ln = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * ((i + 1) >> 2)));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            d0 = d1; d1 = d2;
+            l4 = ln;
+          }
+          s[15] = __builtin_amdgcn_exp2f(fmaf(s[15], c2, -l4.w));
+          mfma_v_settle1(dp);
+        }
+        bf16x8 pB[2], dsB[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pB[i >> 3][i & 7] = (__bf16)s[i];
+        {
+          // dV += P^T dO; operands one MFMA ahead (scheduling fences)
+          float4 d4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + kStageRows * 4));   // Delta, rows 0-3
+          bf16x8 cur = trans_operand_x<D>(lds, t0, t1, 0, 0, C::Q_BYTES);
+#pragma unroll
+          for (int m = 0; m < 2 * DB; ++m) {
+            bf16x8 nxt = cur;
+            float4 dn = d4;
+            if (m + 1 < 2 * DB) {
+              nxt = trans_operand_x<D>(lds, t0, t1, (m + 1) >> 1, (m + 1) & 1, C::Q_BYTES);
+              if ((m & 3) == 3) dn = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * ((m + 1) >> 2) + kStageRows * 4));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dVt[m >> 1] = mfma32(cur, pB[m & 1], dVt[m >> 1]);
+            {
+              const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+              float x = s[m] * (dp[m] - dv4[m & 3]);
+              asm volatile("" : "+v"(x));                // formed here, beside the MFMA
+              dsB[m >> 3][m & 7] = (__bf16)x;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+            d4 = dn;
+          }
+        }
+        {
+          // dK += dS^T Q; operands one MFMA ahead
+          bf16x8 cur = trans_operand_x<D>(lds, t0, t1, 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < 2 * DB; ++m) {
+            bf16x8 nxt = cur;
+            if (m + 1 < 2 * DB) {
+              nxt = trans_operand_x<D>(lds, t0, t1, (m + 1) >> 1, (m + 1) & 1, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dKt[m >> 1] = mfma32(cur, dsB[m & 1], dKt[m >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+          }
+        }
+      } else {
       // P and dS of the stage as B operands (zero where the wave sees none of
       // the stage: the dV / dK products below run on every stage, so that
       // the accumulators are updated on one path only)
@@ -406,6 +524,7 @@ __global__ void __launch_bounds__(NWK * 64) __attribute__((amdgpu_waves_per_eu(1
           da = dn;
           qa = qn;
         }
+      }
       }
     }
     s0 = s1;
