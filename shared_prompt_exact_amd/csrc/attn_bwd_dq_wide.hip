@@ -224,6 +224,81 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      if constexpr (DS == 1) {
+        // One wave per SIMD, so only the wave's own vector work can overlap
+        // its matrix work: S^T as one chain, then dP^T as a second chain with
+        // p = exp2(s c - lse2) of one score beside each MFMA; dS of keys 0-7
+        // (k-slot order), then the dQ products of that contraction half with
+        // dS of keys 8-15 formed beside them, then those of the second half.
+        // Operands read two MFMAs ahead (scheduling fences keep them there).
+        static_assert(KTH == 16 && DB == 8, "one element per dP and per dQ MFMA");
+        {
+          bf16x8 k0 = row_operand_x<D>(lds, kbase, 0, KIMM), k1 = row_operand_x<D>(lds, kbase, 1, KIMM);
+#pragma unroll
+          for (int kk = 0; kk < KTH; ++kk) {
+            bf16x8 k2 = k1;
+            if (kk + 2 < KTH) {
+              k2 = row_operand_x<D>(lds, kbase, kk + 2, KIMM);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            s = mfma32(k0, qB[kk], s);
+            __builtin_amdgcn_sched_barrier(0);
+            k0 = k1; k1 = k2;
+          }
+        }
+        if (kind == 2) {
+          // hidden scores become -inf: p = exp2(-inf - lse2) = 0 below
+          int d0 = qpos - kt.pos0 - 4 * hf;
+          int lim0 = (qvalid ? kt.lim : 0) - 4 * hf;
+          asm volatile("" : "+v"(d0), "+v"(lim0));   // no per-element constants hoisted
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kc = 8 * (i >> 2) + (i & 3);
+            const bool vis = ((unsigned)(d0 - kc) < wspan) & (kc < lim0);
+            s[i] = vis ? s[i] : -INFINITY;
+          }
+        }
+        {
+          bf16x8 v0 = row_operand_x<D>(lds, vbase, 0, VIMM), v1 = row_operand_x<D>(lds, vbase, 1, VIMM);
+#pragma unroll
+          for (int kk = 0; kk < KTH; ++kk) {
+            bf16x8 v2 = v1;
+            if (kk + 2 < KTH) {
+              v2 = row_operand_x<D>(lds, vbase, kk + 2, VIMM);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            dp = mfma32(v0, doB[kk], dp);
+            s[kk] = __builtin_amdgcn_exp2f(fmaf(s[kk], c2, -lse2));
+            asm volatile("" : "+v"(s[kk]));             // formed here, beside the MFMA
+            __builtin_amdgcn_sched_barrier(0);
+            v0 = v1; v1 = v2;
+          }
+        }
+        bf16x8 dsB[2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dsB[0][j] = (__bf16)(s[j] * (dp[j] - dlt));
+        constexpr int NX = 2 * DB;
+        bf16x8 c0 = trans_operand_x<D>(lds, tb0, tb1, 0, 0, KIMM);
+        bf16x8 c1 = trans_operand_x<D>(lds, tb0, tb1, 1 % DB, 1 / DB, KIMM);
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+          const int hs = x / DB, db = x % DB;
+          bf16x8 c2n = c1;
+          if (x + 2 < NX) {
+            c2n = trans_operand_x<D>(lds, tb0, tb1, (x + 2) % DB, (x + 2) / DB, KIMM);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          acc[db] = mfma32(c0, dsB[hs], acc[db]);
+          if (hs == 0) {
+            float e = s[8 + db] * (dp[8 + db] - dlt);
+            asm volatile("" : "+v"(e));                 // formed here, beside the MFMA
+            dsB[1][db] = (__bf16)e;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          c0 = c1;
+          c1 = c2n;
+        }
+      } else {
       if (kind != 0) {
         // S^T = K Q^T and dP^T = V dO^T; the operands of k-step kk+2 are read
         // before the MFMAs of step kk (scheduling fences keep them there)
@@ -302,6 +377,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1,
         __builtin_amdgcn_sched_barrier(0);
         c0 = c1;
         c1 = c2n;
+      }
       }
     };
     static_assert(NS == 2 || NS == 3, "ring of two or three, unrolled by its depth");
