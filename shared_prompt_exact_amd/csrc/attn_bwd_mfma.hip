@@ -187,6 +187,9 @@ __global__ void __launch_bounds__(NWK * 64)
   const float c2 = pr.scale * kLog2e;
   const unsigned wspan = pr.W > 0 ? (unsigned)pr.W : 0x7fffffffu;
   const bool stat_wave = wave == NWK - 1;    // also loads the stage's lse2 / delta
+  // operand reads ahead in the S and dP chains, in k-steps (two for dP
+  // need more than the 256 registers of two waves per SIMD)
+  constexpr int SPF = 2, DPF = 1;
 
   // operand bases (bytes from the start of LDS): V rows of this wave's keys;
   // Q / dO rows l32 of stage 0; Q^T / dO^T transposed reads of stage 0; the
@@ -283,17 +286,18 @@ __global__ void __launch_bounds__(NWK * 64)
         {
           // S = Q K^T as one chain (Q operands read one k-step ahead,
           // scheduling fences keep each read before the MFMA it feeds)
-          bf16x8 qa = row_operand_x<D>(lds, qb, 0, 0);
+          bf16x8 qr[SPF];
+#pragma unroll
+          for (int j = 0; j < SPF; ++j) qr[j] = row_operand_x<D>(lds, qb, j, 0);
 #pragma unroll
           for (int kk = 0; kk < KT; ++kk) {
-            bf16x8 qn = qa;
-            if (kk + 1 < KT) {
-              qn = row_operand_x<D>(lds, qb, kk + 1, 0);
+            const bf16x8 qa = qr[kk % SPF];
+            if (kk + SPF < KT) {
+              qr[kk % SPF] = row_operand_x<D>(lds, qb, kk + SPF, 0);
               __builtin_amdgcn_sched_barrier(0);
             }
             s = mfma32(qa, kB[kk], s);
             __builtin_amdgcn_sched_barrier(0);
-            qa = qn;
           }
         }
         if (kind == 2) {
@@ -316,15 +320,22 @@ __global__ void __launch_bounds__(NWK * 64)
           // so this vector work overlaps the wave's own matrix work)
           constexpr int EPM = 16 / KT;
           static_assert(EPM * KT == 16 && EPM <= 4, "whole score elements per dP MFMA");
-          bf16x8 da = row_operand_x<D>(lds, qb, 0, Q_BYTES), vv = row_operand_x<D>(lds, vb, 0, 0);
+          bf16x8 dr[DPF], vr[DPF];
+#pragma unroll
+          for (int j = 0; j < DPF; ++j) {
+            dr[j] = row_operand_x<D>(lds, qb, j, Q_BYTES);
+            vr[j] = row_operand_x<D>(lds, vb, j, 0);
+          }
           float4 l4 = *reinterpret_cast<const float4*>(lds_at(lds, sb4));   // lse2 of rows 0-3 (+4*hf)
 #pragma unroll
           for (int kk = 0; kk < KT; ++kk) {
-            bf16x8 dn = da, vn = vv;
+            const bf16x8 da = dr[kk % DPF], vv = vr[kk % DPF];
             float4 ln = l4;
             if (kk + 1 < KT) {
-              dn = row_operand_x<D>(lds, qb, kk + 1, Q_BYTES);
-              vn = row_operand_x<D>(lds, vb, kk + 1, 0);
+              if (kk + DPF < KT) {
+                dr[kk % DPF] = row_operand_x<D>(lds, qb, kk + DPF, Q_BYTES);
+                vr[kk % DPF] = row_operand_x<D>(lds, vb, kk + DPF, 0);
+              }
               const int gn = (EPM * (kk + 1)) >> 2;           // row group of the next elements
               if (gn != (EPM * kk) >> 2) ln = *reinterpret_cast<const float4*>(lds_at(lds, sb4 + 32u * gn));
               __builtin_amdgcn_sched_barrier(0);
@@ -338,8 +349,6 @@ __global__ void __launch_bounds__(NWK * 64)
               asm volatile("" : "+v"(s[i]));                   // formed here, beside the MFMA
             }
             __builtin_amdgcn_sched_barrier(0);
-            da = dn;
-            vv = vn;
             l4 = ln;
           }
         }
