@@ -58,7 +58,9 @@ struct KvCfg {
 // their lse2 / delta).  Operand addresses come from a few per-lane bases
 // with one XOR per 16-byte chunk and immediate tile offsets (lds_tiles.h);
 // stage loads take a scalar row address plus per-lane offsets fixed for the
-// kernel (rows clamped only on a partial stage).
+// kernel (rows clamped only on a partial stage).  Per stage: S as one MFMA
+// chain, dP as a second with the exponentials beside its MFMAs, the dV
+// products with dS formed beside them, then the dK products.
 template <int D, int NWK, int NS>
 __global__ void __launch_bounds__(NWK * 64)
     bwd_dkdv_lean_kernel(Problem pa, Groups G, KvGroups KG, const uint16_t* __restrict__ q,
@@ -284,7 +286,7 @@ __global__ void __launch_bounds__(NWK * 64)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
         {
-          // S = Q K^T as one chain (Q operands read one k-step ahead,
+          // S = Q K^T as one chain (Q operands read SPF k-steps ahead,
           // scheduling fences keep each read before the MFMA it feeds)
           bf16x8 qr[SPF];
 #pragma unroll
