@@ -23,7 +23,10 @@
 // (a wait covering the MFMA's result latency separates them from their
 // first vector reads).  Operand reads run ahead of the MFMAs behind
 // scheduling fences; Q / dO stages stream through an LDS ring with
-// XOR-derived operand addresses (lds_tiles.h).
+// XOR-derived operand addresses (lds_tiles.h).  Per stage at head dim 256:
+// S as one MFMA chain, dP as a second with the exponentials beside its
+// MFMAs, the dV products with dS formed beside them, then the dK products;
+// at 512 the pair's partial S and dP meet in LDS after both chains.
 #include "kv_items.h"
 #include "lds_tiles.h"
 

@@ -16,7 +16,11 @@
 // chunk and immediate slot offsets, tile loads from a scalar tile address
 // plus per-lane offsets (lds_tiles.h).  At head dim 256, Delta = dO . O of
 // the wave's rows is formed in the prologue and written with LSE * log2(e)
-// for the dK/dV kernel; at 512 both come from their own kernel.
+// for the dK/dV kernel; at 512 both come from their own kernel.  Per key
+// tile at 256: S as one MFMA chain, dP as a second with the exponentials
+// beside its MFMAs, then the dQ products with half of dS formed beside them;
+// at 512 the pair's partial S and dP meet in LDS between the two chains'
+// MFMAs and the vector work.
 #include "lds_tiles.h"
 
 namespace dualkv {
